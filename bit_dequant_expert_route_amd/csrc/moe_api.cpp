@@ -1,0 +1,631 @@
+// moe_api.cpp -- the C ABI of libmoe: argument checks, workspace layout and
+// the sequencing of the gfx950 kernels.  Every check runs before anything is
+// enqueued; no call allocates, copies or synchronises.
+//
+// The layer runs as three launches with no host round trip in between
+// (openclawradar.com (ja), "Flash-MoE: running the 397B parameter Qwen model
+// on a MacBook Pro in pure C/Metal", section "Deferred GPU expert compute":
+// the expert pass is queued without waiting):
+//   K1 router rows + shared-gate dot + shared expert gate/up/SwiGLU
+//   K2 top-K of the logits (every wave) + routed gate/up/SwiGLU
+//   K3 routed (and shared) down projections + combine + residual
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+using namespace moe_impl;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t up256(size_t n) { return (n + 255u) / 256u * 256u; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool dim_ok(int d) { return d >= 64 && d <= kMaxDim && d % kGroup == 0; }
+
+// ---------------------------------------------------------------------------
+// workspace layout for one layer call
+// ---------------------------------------------------------------------------
+struct WsLayout {
+  size_t logits, sigma, h_routed, h_shared, y_shared, x_stage, hres_stage, h_pong, total;
+};
+
+WsLayout ws_layout(const moe_layer_t *L, int T, int n_layers) {
+  WsLayout w;
+  size_t o = 0;
+  const size_t E = L->n_experts, K = L->top_k, I = L->inter, H = L->hidden;
+  const size_t rows_h = (size_t)T * K > (size_t)kMaxTokens ? (size_t)T * K : (size_t)kMaxTokens;
+  w.logits = o; o += up256(4 * (size_t)T * E);
+  w.sigma = o; o += up256(4 * (size_t)T);
+  w.h_routed = o; o += up256(4 * rows_h * I);
+  w.h_shared = o; o += up256(4 * (size_t)T * I);
+  w.y_shared = o; o += up256(4 * (size_t)T * H);
+  w.x_stage = o; o += up256(4 * H);
+  w.hres_stage = o; o += up256(4 * H);
+  w.h_pong = o; o += n_layers > 0 ? up256(4 * H) : 0;
+  w.total = o;
+  return w;
+}
+
+int check_bits(int b, const char *what) {
+  if (b != 4 && b != 2) return fail(MOE_EUNSUPPORTED, "%s = %d: only 4 and 2 are built", what, b);
+  return MOE_OK;
+}
+
+int check_dtype(int d, const char *what) {
+  if (d != MOE_F32 && d != MOE_BF16) return fail(MOE_EUNSUPPORTED, "%s = %d: not MOE_F32/MOE_BF16", what, d);
+  return MOE_OK;
+}
+
+// shapes, flags and weight pointers of a layer
+int check_layer(const moe_layer_t *L) {
+  if (!L) return fail(MOE_EINVAL, "layer is NULL");
+  if (L->group != kGroup) return fail(MOE_EUNSUPPORTED, "group = %d: only 64 is built", L->group);
+  int st;
+  if ((st = check_bits(L->bits_routed, "bits_routed")) != MOE_OK) return st;
+  if ((st = check_bits(L->bits_shared, "bits_shared")) != MOE_OK) return st;
+  if ((st = check_dtype(L->router_dtype, "router_dtype")) != MOE_OK) return st;
+  if ((st = check_dtype(L->gate_dtype, "gate_dtype")) != MOE_OK) return st;
+  if (!dim_ok(L->hidden)) return fail(MOE_EINVAL, "hidden = %d: need a multiple of 64 in [64, 8192]", L->hidden);
+  if (!dim_ok(L->inter)) return fail(MOE_EINVAL, "inter = %d: need a multiple of 64 in [64, 8192]", L->inter);
+  if (L->top_k < 1 || L->top_k > kMaxK) return fail(MOE_EINVAL, "top_k = %d: need 1..8", L->top_k);
+  if (L->n_experts < L->top_k || L->n_experts > kMaxE)
+    return fail(MOE_EINVAL, "n_experts = %d: need top_k..1024", L->n_experts);
+  if (L->renorm_topk != 0 && L->renorm_topk != 1) return fail(MOE_EINVAL, "renorm_topk must be 0 or 1");
+  if (!L->router || !L->shared_gate || !L->experts || !L->shared_expert)
+    return fail(MOE_EINVAL, "a weight pointer of the layer is NULL");
+  if (!aligned(L->router, 16) || !aligned(L->shared_gate, 16))
+    return fail(MOE_EALIGN, "router and shared_gate must be 16-byte aligned");
+  if (!aligned(L->experts, 256) || !aligned(L->shared_expert, 256) || L->expert_stride % 256)
+    return fail(MOE_EALIGN, "expert records and expert_stride must be 256-byte aligned");
+  const size_t rb = moe_expert_bytes(L->hidden, L->inter, L->bits_routed, L->group);
+  if (L->expert_stride < rb)
+    return fail(MOE_EINVAL, "expert_stride %zu < record size %zu", L->expert_stride, rb);
+  return MOE_OK;
+}
+
+int check_tokens(int T) {
+  if (T < 1 || T > kMaxTokens) return fail(MOE_EINVAL, "n_tokens = %d: need 1..64", T);
+  return MOE_OK;
+}
+
+int check_vec(const void *p, const char *what) {
+  if (!p) return fail(MOE_EINVAL, "%s is NULL", what);
+  if (!aligned(p, 16)) return fail(MOE_EALIGN, "%s must be 16-byte aligned", what);
+  return MOE_OK;
+}
+
+int check_ws(void *ws, size_t have, size_t need) {
+  if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, 256)) return fail(MOE_EALIGN, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MOE_EWORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return MOE_OK;
+}
+
+RecOffsets offsets_of(int H, int I, int bits) { return record_offsets(H, I, bits); }
+
+HeadParams head_params(const moe_layer_t *L, int T) {
+  HeadParams h;
+  memset(&h, 0, sizeof h);
+  h.H = L->hidden;
+  h.I = L->inter;
+  h.E = L->n_experts;
+  h.T = T;
+  h.router_dtype = L->router_dtype;
+  h.router = L->router;
+  h.gate_dtype = L->gate_dtype;
+  h.gvec = L->shared_gate;
+  h.bits_shared = L->bits_shared;
+  h.shared_rec = static_cast<const uint8_t *>(L->shared_expert);
+  h.soff = offsets_of(L->hidden, L->inter, L->bits_shared);
+  return h;
+}
+
+#define MOE_TRY_HIP(expr, what)              \
+  do {                                       \
+    hipError_t e_ = (expr);                  \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+// one token through one layer (x given, or x = rmsnorm(h_in + upd) when
+// xsrc == XS_NORM), writes h_out, idx[K], w[K]
+int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in,
+                const uint16_t *upd, const float *h_res, float *h_out, int32_t *idx, float *w,
+                uint8_t *ws, const WsLayout &wl, hipStream_t s) {
+  float *logits = reinterpret_cast<float *>(ws + wl.logits);
+  float *sigma = reinterpret_cast<float *>(ws + wl.sigma);
+  float *h_routed = reinterpret_cast<float *>(ws + wl.h_routed);
+  float *h_shared = reinterpret_cast<float *>(ws + wl.h_shared);
+  float *y_shared = reinterpret_cast<float *>(ws + wl.y_shared);
+  float *x_stage = reinterpret_cast<float *>(ws + wl.x_stage);
+  float *hres_stage = reinterpret_cast<float *>(ws + wl.hres_stage);
+
+  // K1
+  HeadParams hp = head_params(L, 1);
+  hp.xsrc = xsrc;
+  hp.x = x;
+  hp.h_in = h_in;
+  hp.upd = upd;
+  hp.logits = logits;
+  hp.sigma = sigma;
+  if (xsrc == XS_NORM) {
+    hp.x_out = x_stage;
+    hp.hres_out = hres_stage;
+  }
+  hp.h_shared = h_shared;
+  hp.n_shared_waves = 1;  // launcher sizes it
+  MOE_TRY_HIP(launch_head(hp, s), "router/shared launch");
+
+  // K2
+  GateUpParams gp;
+  memset(&gp, 0, sizeof gp);
+  gp.H = L->hidden;
+  gp.I = L->inter;
+  gp.E = L->n_experts;
+  gp.K = L->top_k;
+  gp.renorm = L->renorm_topk;
+  gp.bits = L->bits_routed;
+  gp.experts = static_cast<const uint8_t *>(L->experts);
+  gp.stride = L->expert_stride;
+  gp.shared_rec = static_cast<const uint8_t *>(L->shared_expert);
+  gp.shared_ok = L->bits_shared == L->bits_routed;
+  gp.off = offsets_of(L->hidden, L->inter, L->bits_routed);
+  gp.soff = offsets_of(L->hidden, L->inter, L->bits_shared);
+  gp.ids = nullptr;
+  gp.n = L->top_k;
+  gp.logits = logits;
+  gp.idx_out = idx;
+  gp.w_out = w;
+  gp.xsrc = xsrc == XS_BF16 ? XS_BF16 : XS_F32;
+  gp.x = xsrc == XS_NORM ? static_cast<const void *>(x_stage) : x;
+  gp.h_out = h_routed;
+  MOE_TRY_HIP(launch_gateup(gp, s), "routed gate/up launch");
+
+  // K3 (+ the shared down in its own launch when its width differs)
+  DownParams dp;
+  memset(&dp, 0, sizeof dp);
+  dp.H = L->hidden;
+  dp.I = L->inter;
+  dp.E = L->n_experts;
+  dp.experts = gp.experts;
+  dp.stride = gp.stride;
+  dp.shared_rec = gp.shared_rec;
+  dp.off = gp.off;
+  dp.soff = gp.soff;
+  dp.shared_ok = 1;
+  const bool same = L->bits_shared == L->bits_routed;
+  if (!same) {
+    // shared expert of another width: its down projection runs on its own
+    // (a null id list selects the shared record) and K3 adds sigma * y_shared
+    DownParams sp = dp;
+    sp.combine = 0;
+    sp.bits_r = L->bits_shared;
+    sp.ids = nullptr;
+    sp.n = 1;
+    sp.h = h_shared;
+    sp.y = y_shared;
+    MOE_TRY_HIP(launch_down(sp, s), "shared down launch");
+  }
+  dp.combine = 1;
+  dp.bits_r = L->bits_routed;
+  dp.bits_s = L->bits_shared;
+  dp.idx = idx;
+  dp.w = w;
+  dp.K = L->top_k;
+  dp.sigma = sigma;
+  dp.h_routed = h_routed;
+  dp.h_shared = same ? h_shared : nullptr;
+  dp.y = same ? nullptr : y_shared;
+  dp.h_res = xsrc == XS_NORM ? hres_stage : h_res;
+  dp.out = h_out;
+  MOE_TRY_HIP(launch_down(dp, s), "down/combine launch");
+  return MOE_OK;
+}
+
+int expert_forward(const moe_layer_t *L, int bits, moe_dtype x_dtype, const void *x,
+                   const int32_t *ids, int n, float *y, float *h, void *ws, size_t ws_bytes,
+                   void *stream) {
+  int st;
+  if ((st = check_layer(L)) != MOE_OK) return st;
+  if (L->bits_routed != bits)
+    return fail(MOE_EUNSUPPORTED, "layer bits_routed = %d but this entry point is %d-bit", L->bits_routed, bits);
+  if ((st = check_dtype(x_dtype, "x_dtype")) != MOE_OK) return st;
+  if ((st = check_vec(x, "x")) != MOE_OK) return st;
+  if ((st = check_vec(y, "y")) != MOE_OK) return st;
+  if (!ids) return fail(MOE_EINVAL, "expert_ids is NULL");
+  if (!aligned(ids, 4)) return fail(MOE_EALIGN, "expert_ids must be 4-byte aligned");
+  if (n < 1 || n > kMaxTokens) return fail(MOE_EINVAL, "n = %d: need 1..64", n);
+  if (h && !aligned(h, 16)) return fail(MOE_EALIGN, "h must be 16-byte aligned");
+  const WsLayout wl = ws_layout(L, 1, 0);
+  if ((st = check_ws(ws, ws_bytes, wl.total)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  float *hbuf = h ? h : reinterpret_cast<float *>(wsb + wl.h_routed);
+
+  GateUpParams gp;
+  memset(&gp, 0, sizeof gp);
+  gp.H = L->hidden;
+  gp.I = L->inter;
+  gp.E = L->n_experts;
+  gp.K = L->top_k;
+  gp.bits = bits;
+  gp.experts = static_cast<const uint8_t *>(L->experts);
+  gp.stride = L->expert_stride;
+  gp.shared_rec = static_cast<const uint8_t *>(L->shared_expert);
+  gp.shared_ok = L->bits_shared == bits;
+  gp.off = offsets_of(L->hidden, L->inter, bits);
+  gp.soff = offsets_of(L->hidden, L->inter, L->bits_shared);
+  gp.ids = ids;
+  gp.n = n;
+  gp.xsrc = x_dtype == MOE_BF16 ? XS_BF16 : XS_F32;
+  gp.x = x;
+  gp.h_out = hbuf;
+  MOE_TRY_HIP(launch_gateup(gp, s), "gate/up launch");
+
+  DownParams dp;
+  memset(&dp, 0, sizeof dp);
+  dp.H = L->hidden;
+  dp.I = L->inter;
+  dp.E = L->n_experts;
+  dp.bits_r = bits;
+  dp.bits_s = L->bits_shared;
+  dp.experts = gp.experts;
+  dp.stride = gp.stride;
+  dp.shared_rec = gp.shared_rec;
+  dp.off = gp.off;
+  dp.soff = gp.soff;
+  dp.combine = 0;
+  dp.ids = ids;
+  dp.n = n;
+  dp.h = hbuf;
+  dp.y = y;
+  dp.shared_ok = gp.shared_ok;
+  MOE_TRY_HIP(launch_down(dp, s), "down launch");
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace moe_impl {
+RecOffsets record_offsets(int hidden, int inter, int bits) {
+  RecOffsets r;
+  const size_t gc = (size_t)inter * hidden * bits / 8;
+  const size_t dc = (size_t)hidden * inter * bits / 8;
+  const size_t gs = (size_t)inter * (hidden / kGroup) * 4;
+  const size_t ds = (size_t)hidden * (inter / kGroup) * 4;
+  r.gate_codes = 0;
+  r.up_codes = r.gate_codes + up256(gc);
+  r.down_codes = r.up_codes + up256(gc);
+  r.gate_sb = r.down_codes + up256(dc);
+  r.up_sb = r.gate_sb + up256(gs);
+  r.down_sb = r.up_sb + up256(gs);
+  r.total = r.down_sb + up256(ds);
+  return r;
+}
+}  // namespace moe_impl
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char *moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported configuration";
+    case MOE_EALIGN: return "misaligned pointer or stride";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+int moe_abi_version(void) { return 1; }
+
+size_t moe_qmatrix_bytes(int rows, int cols, int bits, int group) {
+  if (group != kGroup || (bits != 4 && bits != 2) || rows < 1 || cols < kGroup || cols % kGroup) return 0;
+  return up256((size_t)rows * cols * bits / 8) + up256((size_t)rows * (cols / kGroup) * 4);
+}
+
+size_t moe_expert_bytes(int hidden, int inter, int bits, int group) {
+  if (group != kGroup || (bits != 4 && bits != 2) || !dim_ok(hidden) || !dim_ok(inter)) return 0;
+  return record_offsets(hidden, inter, bits).total;
+}
+
+int moe_expert_offsets(int hidden, int inter, int bits, int group, size_t out[6]) {
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  if (moe_expert_bytes(hidden, inter, bits, group) == 0)
+    return fail(MOE_EINVAL, "invalid record shape (%d, %d, %d bits, group %d)", hidden, inter, bits, group);
+  const RecOffsets r = record_offsets(hidden, inter, bits);
+  out[0] = r.gate_codes; out[1] = r.up_codes; out[2] = r.down_codes;
+  out[3] = r.gate_sb; out[4] = r.up_sb; out[5] = r.down_sb;
+  return MOE_OK;
+}
+
+size_t moe_layer_workspace_bytes(const moe_layer_t *L, int n_tokens) {
+  if (!L || n_tokens < 1 || n_tokens > kMaxTokens) return 0;
+  if (L->top_k < 1 || L->top_k > kMaxK || L->n_experts < 1 || !dim_ok(L->hidden) || !dim_ok(L->inter)) return 0;
+  return ws_layout(L, n_tokens, 0).total;
+}
+
+size_t moe_stack_workspace_bytes(const moe_layer_t *L, int n_layers) {
+  if (!L || n_layers < 1) return 0;
+  if (L->top_k < 1 || L->top_k > kMaxK || L->n_experts < 1 || !dim_ok(L->hidden) || !dim_ok(L->inter)) return 0;
+  return ws_layout(L, 1, n_layers).total;
+}
+
+int moe_route(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void *x,
+              int32_t *topk_idx, float *topk_w, float *shared_sigma, float *logits,
+              void *ws, size_t ws_bytes, void *stream) {
+  int st;
+  if ((st = check_layer(L)) != MOE_OK) return st;
+  if ((st = check_tokens(n_tokens)) != MOE_OK) return st;
+  if ((st = check_dtype(x_dtype, "x_dtype")) != MOE_OK) return st;
+  if ((st = check_vec(x, "x")) != MOE_OK) return st;
+  if (!topk_idx || !topk_w || !shared_sigma) return fail(MOE_EINVAL, "an output pointer is NULL");
+  if (!aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(shared_sigma, 4))
+    return fail(MOE_EALIGN, "outputs must be 4-byte aligned");
+  if (logits && !aligned(logits, 4)) return fail(MOE_EALIGN, "logits must be 4-byte aligned");
+  const WsLayout wl = ws_layout(L, n_tokens, 0);
+  if ((st = check_ws(ws, ws_bytes, wl.total)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  float *lg = logits ? logits : reinterpret_cast<float *>(wsb + wl.logits);
+  HeadParams hp = head_params(L, n_tokens);
+  hp.xsrc = x_dtype == MOE_BF16 ? XS_BF16 : XS_F32;
+  hp.x = x;
+  hp.logits = lg;
+  hp.sigma = shared_sigma;
+  hp.n_shared_waves = 0;
+  MOE_TRY_HIP(launch_head(hp, s), "router launch");
+  TopkParams tp;
+  tp.logits = lg;
+  tp.T = n_tokens;
+  tp.E = L->n_experts;
+  tp.K = L->top_k;
+  tp.renorm = L->renorm_topk;
+  tp.idx = topk_idx;
+  tp.w = topk_w;
+  MOE_TRY_HIP(launch_topk(tp, s), "top-K launch");
+  return MOE_OK;
+}
+
+int moe_expert_forward_q4(const moe_layer_t *L, moe_dtype x_dtype, const void *x,
+                          const int32_t *expert_ids, int n, float *y, float *h, void *ws,
+                          size_t ws_bytes, void *stream) {
+  return expert_forward(L, 4, x_dtype, x, expert_ids, n, y, h, ws, ws_bytes, stream);
+}
+
+int moe_expert_forward_q2(const moe_layer_t *L, moe_dtype x_dtype, const void *x,
+                          const int32_t *expert_ids, int n, float *y, float *h, void *ws,
+                          size_t ws_bytes, void *stream) {
+  return expert_forward(L, 2, x_dtype, x, expert_ids, n, y, h, ws, ws_bytes, stream);
+}
+
+int moe_combine(int hidden, int n_routed, const float *h_res, const float *y, const float *w,
+                const float *y_shared, const float *shared_sigma, float *h_out, void *stream) {
+  if (hidden < 1 || hidden > kMaxDim) return fail(MOE_EINVAL, "hidden = %d out of range", hidden);
+  if (n_routed < 0 || n_routed > kMaxK * kMaxTokens) return fail(MOE_EINVAL, "n_routed = %d out of range", n_routed);
+  int st;
+  if ((st = check_vec(h_res, "h_res")) != MOE_OK) return st;
+  if ((st = check_vec(y_shared, "y_shared")) != MOE_OK) return st;
+  if ((st = check_vec(h_out, "h_out")) != MOE_OK) return st;
+  if (n_routed > 0) {
+    if ((st = check_vec(y, "y")) != MOE_OK) return st;
+    if (!w) return fail(MOE_EINVAL, "w is NULL");
+  }
+  if (!shared_sigma) return fail(MOE_EINVAL, "shared_sigma is NULL");
+  CombineParams p;
+  p.H = hidden;
+  p.K = n_routed;
+  p.h_res = h_res;
+  p.y = y;
+  p.w = w;
+  p.y_shared = y_shared;
+  p.sigma = shared_sigma;
+  p.out = h_out;
+  MOE_TRY_HIP(launch_combine(p, static_cast<hipStream_t>(stream)), "combine launch");
+  return MOE_OK;
+}
+
+int moe_layer_decode(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void *x,
+                     const float *h_res, float *h_out, int32_t *topk_idx, float *topk_w,
+                     void *ws, size_t ws_bytes, void *stream) {
+  int st;
+  if ((st = check_layer(L)) != MOE_OK) return st;
+  if ((st = check_tokens(n_tokens)) != MOE_OK) return st;
+  if ((st = check_dtype(x_dtype, "x_dtype")) != MOE_OK) return st;
+  if ((st = check_vec(x, "x")) != MOE_OK) return st;
+  if ((st = check_vec(h_res, "h_res")) != MOE_OK) return st;
+  if ((st = check_vec(h_out, "h_out")) != MOE_OK) return st;
+  if (h_out == h_res) return fail(MOE_EINVAL, "h_out may not alias h_res");
+  if (!topk_idx || !topk_w) return fail(MOE_EINVAL, "topk_idx / topk_w is NULL");
+  if (!aligned(topk_idx, 4) || !aligned(topk_w, 4)) return fail(MOE_EALIGN, "topk outputs must be 4-byte aligned");
+  const WsLayout wl = ws_layout(L, n_tokens, 0);
+  if ((st = check_ws(ws, ws_bytes, wl.total)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int xsrc = x_dtype == MOE_BF16 ? XS_BF16 : XS_F32;
+  const size_t xes = x_dtype == MOE_BF16 ? 2 : 4;
+  const size_t H = L->hidden, K = L->top_k;
+  for (int t = 0; t < n_tokens; ++t) {
+    st = layer_token(L, xsrc, static_cast<const uint8_t *>(x) + t * H * xes, nullptr, nullptr,
+                     h_res + t * H, h_out + t * H, topk_idx + t * K, topk_w + t * K,
+                     static_cast<uint8_t *>(ws), wl, s);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+int moe_layer_ws_view(const moe_layer_t *L, int n_tokens, void *ws, size_t ws_bytes,
+                      moe_ws_view *view) {
+  int st;
+  if ((st = check_layer(L)) != MOE_OK) return st;
+  if ((st = check_tokens(n_tokens)) != MOE_OK) return st;
+  if (!view) return fail(MOE_EINVAL, "view is NULL");
+  const WsLayout wl = ws_layout(L, n_tokens, 0);
+  if ((st = check_ws(ws, ws_bytes, wl.total)) != MOE_OK) return st;
+  uint8_t *b = static_cast<uint8_t *>(ws);
+  view->logits = reinterpret_cast<float *>(b + wl.logits);
+  view->sigma = reinterpret_cast<float *>(b + wl.sigma);
+  view->h_routed = reinterpret_cast<float *>(b + wl.h_routed);
+  view->h_shared = reinterpret_cast<float *>(b + wl.h_shared);
+  return MOE_OK;
+}
+
+int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *updates_bf16,
+                     float *h, int32_t *idx_log, float *w_log, void *ws, size_t ws_bytes,
+                     void *stream) {
+  if (!layers) return fail(MOE_EINVAL, "layers is NULL");
+  if (n_layers < 1) return fail(MOE_EINVAL, "n_layers = %d", n_layers);
+  int st;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_layer(&layers[l])) != MOE_OK) return st;
+    const moe_layer_t &a = layers[0], &b = layers[l];
+    if (a.hidden != b.hidden || a.inter != b.inter || a.n_experts != b.n_experts ||
+        a.top_k != b.top_k || a.bits_routed != b.bits_routed || a.bits_shared != b.bits_shared ||
+        a.router_dtype != b.router_dtype || a.gate_dtype != b.gate_dtype)
+      return fail(MOE_EINVAL, "layer %d differs in shape or format from layer 0", l);
+  }
+  if ((st = check_vec(h, "h")) != MOE_OK) return st;
+  if (updates_bf16 && !aligned(updates_bf16, 16)) return fail(MOE_EALIGN, "updates must be 16-byte aligned");
+  if (!idx_log || !w_log) return fail(MOE_EINVAL, "idx_log / w_log is NULL");
+  if (!aligned(idx_log, 4) || !aligned(w_log, 4)) return fail(MOE_EALIGN, "logs must be 4-byte aligned");
+  const moe_layer_t *L = &layers[0];
+  const WsLayout wl = ws_layout(L, 1, n_layers);
+  if ((st = check_ws(ws, ws_bytes, wl.total)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  float *pong = reinterpret_cast<float *>(wsb + wl.h_pong);
+  const size_t H = L->hidden, K = L->top_k;
+  float *cur = h, *nxt = pong;
+  for (int l = 0; l < n_layers; ++l) {
+    const uint16_t *u = updates_bf16 ? updates_bf16 + (size_t)l * H : nullptr;
+    st = layer_token(&layers[l], XS_NORM, nullptr, cur, u, nullptr, nxt, idx_log + l * K,
+                     w_log + l * K, wsb, wl, s);
+    if (st != MOE_OK) return st;
+    float *t = cur;
+    cur = nxt;
+    nxt = t;
+  }
+  if (cur != h) MOE_TRY_HIP(launch_copy_f32(h, cur, L->hidden, s), "copy launch");
+  return MOE_OK;
+}
+
+struct moe_graph_s {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+int moe_graph_capture_begin(void *stream) {
+  if (!stream) return fail(MOE_EINVAL, "capture needs a non-NULL stream");
+  MOE_TRY_HIP(hipStreamBeginCapture(static_cast<hipStream_t>(stream), hipStreamCaptureModeThreadLocal),
+              "hipStreamBeginCapture");
+  return MOE_OK;
+}
+
+int moe_graph_capture_end(void *stream, moe_graph_t *out) {
+  if (!stream || !out) return fail(MOE_EINVAL, "stream / out is NULL");
+  hipGraph_t g = nullptr;
+  MOE_TRY_HIP(hipStreamEndCapture(static_cast<hipStream_t>(stream), &g), "hipStreamEndCapture");
+  hipGraphExec_t ex = nullptr;
+  hipError_t e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  moe_graph_s *r = new moe_graph_s{g, ex};
+  *out = r;
+  return MOE_OK;
+}
+
+int moe_graph_create_stack(const moe_layer_t *layers, int n_layers, const uint16_t *updates_bf16,
+                           float *h, int32_t *idx_log, float *w_log, void *ws, size_t ws_bytes,
+                           void *stream, moe_graph_t *out) {
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  int st = moe_graph_capture_begin(stream);
+  if (st != MOE_OK) return st;
+  st = moe_stack_decode(layers, n_layers, updates_bf16, h, idx_log, w_log, ws, ws_bytes, stream);
+  if (st != MOE_OK) {
+    hipGraph_t g = nullptr;
+    (void)hipStreamEndCapture(static_cast<hipStream_t>(stream), &g);
+    if (g) (void)hipGraphDestroy(g);
+    return st;
+  }
+  return moe_graph_capture_end(stream, out);
+}
+
+int moe_graph_launch(moe_graph_t g, void *stream) {
+  if (!g) return fail(MOE_EINVAL, "graph is NULL");
+  MOE_TRY_HIP(hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)), "hipGraphLaunch");
+  return MOE_OK;
+}
+
+int moe_graph_destroy(moe_graph_t g) {
+  if (!g) return fail(MOE_EINVAL, "graph is NULL");
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
+  delete g;
+  return MOE_OK;
+}
+
+int moe_fill_experts(void *dst, size_t stride, int n, uint64_t seed, int layer, int first_expert,
+                     int hidden, int inter, int bits, double scale_lo, double scale_hi,
+                     double bias_lo, double bias_hi, void *stream) {
+  if (!dst) return fail(MOE_EINVAL, "dst is NULL");
+  if (!aligned(dst, 256) || stride % 256) return fail(MOE_EALIGN, "dst and stride must be 256-byte aligned");
+  int st;
+  if ((st = check_bits(bits, "bits")) != MOE_OK) return st;
+  if (!dim_ok(hidden) || !dim_ok(inter)) return fail(MOE_EINVAL, "hidden/inter must be multiples of 64 in [64, 8192]");
+  if (n < 1 || n > 65535) return fail(MOE_EINVAL, "n = %d: need 1..65535", n);
+  const RecOffsets off = record_offsets(hidden, inter, bits);
+  if (n > 1 && stride < off.total) return fail(MOE_EINVAL, "stride %zu < record size %zu", stride, off.total);
+  if (!(scale_lo <= scale_hi) || !(bias_lo <= bias_hi)) return fail(MOE_EINVAL, "empty value range");
+  FillParams p;
+  p.dst = static_cast<uint8_t *>(dst);
+  p.stride = stride;
+  p.n = n;
+  p.seed = seed;
+  p.layer = layer;
+  p.first_expert = first_expert;
+  p.H = hidden;
+  p.I = inter;
+  p.bits = bits;
+  p.scale_lo = scale_lo;
+  p.scale_hi = scale_hi;
+  p.bias_lo = bias_lo;
+  p.bias_hi = bias_hi;
+  p.off = off;
+  MOE_TRY_HIP(launch_fill(p, static_cast<hipStream_t>(stream)), "fill launch");
+  return MOE_OK;
+}
+
+int moe_zero(void *ptr, size_t bytes, void *stream) {
+  if (!ptr) return fail(MOE_EINVAL, "ptr is NULL");
+  if (!aligned(ptr, 16)) return fail(MOE_EALIGN, "ptr must be 16-byte aligned");
+  MOE_TRY_HIP(launch_zero(ptr, bytes, static_cast<hipStream_t>(stream)), "zero launch");
+  return MOE_OK;
+}
+
+}  // extern "C"

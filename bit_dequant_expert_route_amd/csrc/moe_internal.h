@@ -1,0 +1,153 @@
+// moe_internal.h -- parameter blocks and launchers shared by the C ABI layer
+// (moe_api.cpp) and the gfx950 kernels (moe_kernels.hip).  Library-internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe_impl {
+
+constexpr int kGroup = 64;
+constexpr int kMaxK = 8;
+constexpr int kMaxE = 1024;
+constexpr int kMaxDim = 8192;
+constexpr int kMaxTokens = 64;
+constexpr int kSharedId = -1;          // MOE_SHARED
+constexpr int kBlock = 256;            // threads per workgroup (4 waves)
+
+// where a kernel reads its activation vector from
+enum XSrc : int {
+  XS_BF16 = 0,   // bf16 [H] in global memory
+  XS_F32 = 1,    // fp32 [H] in global memory
+  XS_NORM = 2,   // x = rmsnorm(h + u), computed per workgroup into LDS
+};
+
+// byte offsets of a record's sections
+struct RecOffsets {
+  size_t gate_codes, up_codes, down_codes, gate_sb, up_sb, down_sb, total;
+};
+RecOffsets record_offsets(int hidden, int inter, int bits);
+
+// ---------------------------------------------------------------------------
+// K1: router rows + shared-gate dot + (optionally) the shared expert's
+//     gate/up/SwiGLU rows.  One launch per layer.
+// ---------------------------------------------------------------------------
+struct HeadParams {
+  int H, I, E, T;                 // T tokens (router + gate only when T > 1)
+  int router_dtype;               // 0 f32, 1 bf16
+  const void *router;             // [E][H]
+  int gate_dtype;
+  const void *gvec;               // [H]
+  int xsrc;                       // XSrc
+  const void *x;                  // [T][H] (XS_BF16 / XS_F32)
+  const float *h_in;              // XS_NORM: [H] residual before the update
+  const uint16_t *upd;            // XS_NORM: [H] bf16 update, may be null
+  float *logits;                  // [T][E]
+  float *sigma;                   // [T]
+  float *x_out;                   // XS_NORM: fp32 x written by workgroup 0
+  float *hres_out;                // XS_NORM: fp32 h + u written by workgroup 0
+  // shared expert (only when n_shared_waves > 0)
+  const uint8_t *shared_rec;
+  int bits_shared;
+  RecOffsets soff;
+  float *h_shared;                // [I]
+  int n_router_blocks;
+  int n_shared_waves;
+  int shared_rows_per_wave;
+};
+hipError_t launch_head(const HeadParams &p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// top-K + softmax weights from logits (stand-alone routing entry point)
+// ---------------------------------------------------------------------------
+struct TopkParams {
+  const float *logits;  // [T][E]
+  int T, E, K, renorm;
+  int32_t *idx;         // [T][K]
+  float *w;             // [T][K]
+};
+hipError_t launch_topk(const TopkParams &p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// K2: gate/up + SwiGLU for a list of experts (explicit ids, or the top-K of
+//     device logits computed by every wave)
+// ---------------------------------------------------------------------------
+struct GateUpParams {
+  int H, I, E, K, renorm;
+  int bits;                       // width of the listed experts
+  const uint8_t *experts;
+  size_t stride;
+  const uint8_t *shared_rec;
+  int shared_ok;                  // shared record has this width
+  RecOffsets off;                 // routed record offsets (bits)
+  RecOffsets soff;                // shared record offsets (bits_shared)
+  const int32_t *ids;             // [n] explicit ids, or null -> top-K of logits
+  int n;                          // list length (== K in top-K mode)
+  const float *logits;            // [E] (top-K mode)
+  int32_t *idx_out;               // top-K mode: written by wave 0 (may be null)
+  float *w_out;
+  int xsrc;                       // XS_BF16 or XS_F32
+  const void *x;                  // [H]
+  float *h_out;                   // [n][I]
+  int rows_per_wave;
+  int waves_per_expert;
+};
+hipError_t launch_gateup(const GateUpParams &p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// K3: down projection.  COMBINE: every wave takes all K routed experts (ids
+//     and weights from device memory) plus the shared expert (weight sigma)
+//     for its output rows and writes out = h_res + sum.  Y: one expert per
+//     wave, y[slot][o] written.
+// ---------------------------------------------------------------------------
+struct DownParams {
+  int H, I, E;
+  int bits_r, bits_s;
+  const uint8_t *experts;
+  size_t stride;
+  const uint8_t *shared_rec;
+  RecOffsets off, soff;
+  int combine;                    // 1 COMBINE, 0 Y
+  // COMBINE
+  const int32_t *idx;             // [K]
+  const float *w;                 // [K]
+  int K;
+  const float *sigma;             // [1]
+  const float *h_routed;          // [K][I]
+  const float *h_shared;          // [I]
+  const float *h_res;             // [H]
+  float *out;                     // [H]
+  // Y
+  const int32_t *ids;             // [n]
+  int n;
+  const float *h;                 // [n][I]
+  float *y;                       // [n][H]
+  int shared_ok;
+  int rows_per_wave;
+  int waves_per_expert;           // Y mode
+};
+hipError_t launch_down(const DownParams &p, hipStream_t s);
+
+struct CombineParams {
+  int H, K;
+  const float *h_res, *y, *w, *y_shared, *sigma;
+  float *out;
+};
+hipError_t launch_combine(const CombineParams &p, hipStream_t s);
+
+struct FillParams {
+  uint8_t *dst;
+  size_t stride;
+  int n;
+  uint64_t seed;
+  int layer, first_expert, H, I, bits;
+  double scale_lo, scale_hi, bias_lo, bias_hi;
+  RecOffsets off;
+};
+hipError_t launch_fill(const FillParams &p, hipStream_t s);
+
+hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t s);
+hipError_t launch_copy_f32(float *dst, const float *src, int n, hipStream_t s);
+
+}  // namespace moe_impl

@@ -1,0 +1,295 @@
+"""ctypes binding of libmoe (include/moe.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+Tensors are torch CUDA tensors (torch provides device memory and streams);
+each call passes `tensor.data_ptr()` and the current stream's handle.  The
+library must have been built (`python -m bit_dequant_expert_route_amd.build`);
+importing this module without it raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("MOE_LIB", os.path.join(HERE, "libmoe.so"))
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SHARED = -1
+GROUP = 64
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        super().__init__(f"{fn}: {detail} (status {status})")
+        self.status = status
+
+
+class LayerStruct(C.Structure):
+    _fields_ = [
+        ("hidden", C.c_int), ("inter", C.c_int), ("n_experts", C.c_int), ("top_k", C.c_int),
+        ("group", C.c_int), ("bits_routed", C.c_int), ("bits_shared", C.c_int),
+        ("renorm_topk", C.c_int),
+        ("router_dtype", C.c_int), ("router", C.c_void_p),
+        ("gate_dtype", C.c_int), ("shared_gate", C.c_void_p),
+        ("experts", C.c_void_p), ("expert_stride", C.c_size_t),
+        ("shared_expert", C.c_void_p),
+    ]
+
+
+class WsView(C.Structure):
+    _fields_ = [("logits", C.c_void_p), ("sigma", C.c_void_p),
+                ("h_routed", C.c_void_p), ("h_shared", C.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libmoe is not built ({LIB_PATH} missing): run "
+                          "python -m bit_dequant_expert_route_amd.build")
+    lib = C.CDLL(LIB_PATH)
+    P, I, Z, V = C.c_void_p, C.c_int, C.c_size_t, None
+    sig = {
+        "moe_strerror": (C.c_char_p, [I]),
+        "moe_last_error": (C.c_char_p, []),
+        "moe_abi_version": (I, []),
+        "moe_qmatrix_bytes": (Z, [I, I, I, I]),
+        "moe_expert_bytes": (Z, [I, I, I, I]),
+        "moe_expert_offsets": (I, [I, I, I, I, C.POINTER(C.c_size_t)]),
+        "moe_layer_workspace_bytes": (Z, [C.POINTER(LayerStruct), I]),
+        "moe_stack_workspace_bytes": (Z, [C.POINTER(LayerStruct), I]),
+        "moe_route": (I, [C.POINTER(LayerStruct), I, I, P, P, P, P, P, P, Z, P]),
+        "moe_expert_forward_q4": (I, [C.POINTER(LayerStruct), I, P, P, I, P, P, P, Z, P]),
+        "moe_expert_forward_q2": (I, [C.POINTER(LayerStruct), I, P, P, I, P, P, P, Z, P]),
+        "moe_combine": (I, [I, I, P, P, P, P, P, P, P]),
+        "moe_layer_decode": (I, [C.POINTER(LayerStruct), I, I, P, P, P, P, P, P, Z, P]),
+        "moe_layer_ws_view": (I, [C.POINTER(LayerStruct), I, P, Z, C.POINTER(WsView)]),
+        "moe_stack_decode": (I, [C.POINTER(LayerStruct), I, P, P, P, P, P, Z, P]),
+        "moe_graph_capture_begin": (I, [P]),
+        "moe_graph_capture_end": (I, [P, C.POINTER(P)]),
+        "moe_graph_create_stack": (I, [C.POINTER(LayerStruct), I, P, P, P, P, P, Z, P, C.POINTER(P)]),
+        "moe_graph_launch": (I, [P, P]),
+        "moe_graph_destroy": (I, [P]),
+        "moe_fill_experts": (I, [P, Z, I, C.c_uint64, I, I, I, I, I, C.c_double, C.c_double,
+                                 C.c_double, C.c_double, P]),
+        "moe_zero": (I, [P, Z, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+lib = _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/moe.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status: int, fn: str):
+    if status != MOE_OK:
+        raise MoeError(status, fn, _lib.moe_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# sizes
+# ---------------------------------------------------------------------------
+def expert_bytes(hidden: int, inter: int, bits: int) -> int:
+    return int(_lib.moe_expert_bytes(hidden, inter, bits, GROUP))
+
+
+def qmatrix_bytes(rows: int, cols: int, bits: int) -> int:
+    return int(_lib.moe_qmatrix_bytes(rows, cols, bits, GROUP))
+
+
+def expert_offsets(hidden: int, inter: int, bits: int) -> list[int]:
+    out = (C.c_size_t * 6)()
+    _check(_lib.moe_expert_offsets(hidden, inter, bits, GROUP, out), "moe_expert_offsets")
+    return list(out)
+
+
+# ---------------------------------------------------------------------------
+# layer description
+# ---------------------------------------------------------------------------
+class Layer:
+    """A MoE layer's shapes and weights (torch CUDA tensors it keeps alive)."""
+
+    def __init__(self, *, hidden, inter, n_experts, top_k, bits_routed, bits_shared,
+                 renorm, router, gate_vec, experts, expert_stride, shared_expert):
+        self.router, self.gate_vec = router, gate_vec
+        self.experts, self.shared_expert = experts, shared_expert
+        self.s = LayerStruct(hidden, inter, n_experts, top_k, GROUP, bits_routed, bits_shared,
+                             int(renorm), _dtype_code(router), _ptr(router),
+                             _dtype_code(gate_vec), _ptr(gate_vec),
+                             _ptr(experts), expert_stride, _ptr(shared_expert))
+
+    def __getattr__(self, name):
+        s = self.__dict__.get("s")
+        if s is not None and name in dict(LayerStruct._fields_):
+            return getattr(s, name)
+        raise AttributeError(name)
+
+    def workspace_bytes(self, n_tokens: int = 1) -> int:
+        return int(_lib.moe_layer_workspace_bytes(C.byref(self.s), n_tokens))
+
+    def workspace(self, n_tokens: int = 1) -> torch.Tensor:
+        return torch.empty(self.workspace_bytes(n_tokens), dtype=torch.uint8, device="cuda")
+
+
+def _ws(layer: Layer, ws, n_tokens: int):
+    if ws is None:
+        ws = layer.workspace(n_tokens)
+    return ws, _ptr(ws), ws.numel()
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def route(layer: Layer, x, topk_idx, topk_w, sigma, logits=None, ws=None, stream=None):
+    T = x.shape[0] if x.dim() == 2 else 1
+    ws, wp, wb = _ws(layer, ws, T)
+    _check(_lib.moe_route(C.byref(layer.s), T, _dtype_code(x), _ptr(x), _ptr(topk_idx),
+                          _ptr(topk_w), _ptr(sigma), _ptr(logits), wp, wb, _stream(stream)),
+           "moe_route")
+
+
+def expert_forward(layer: Layer, bits: int, x, ids, y, h=None, ws=None, stream=None):
+    ws, wp, wb = _ws(layer, ws, 1)
+    fn = _lib.moe_expert_forward_q4 if bits == 4 else _lib.moe_expert_forward_q2
+    _check(fn(C.byref(layer.s), _dtype_code(x), _ptr(x), _ptr(ids), ids.numel(), _ptr(y),
+              _ptr(h), wp, wb, _stream(stream)), f"moe_expert_forward_q{bits}")
+
+
+def combine(h_res, y, w, y_shared, sigma, out, stream=None):
+    _check(_lib.moe_combine(h_res.numel(), w.numel(), _ptr(h_res), _ptr(y), _ptr(w),
+                            _ptr(y_shared), _ptr(sigma), _ptr(out), _stream(stream)),
+           "moe_combine")
+
+
+def layer_decode(layer: Layer, x, h_res, h_out, topk_idx, topk_w, ws=None, stream=None):
+    T = x.shape[0] if x.dim() == 2 else 1
+    ws, wp, wb = _ws(layer, ws, T)
+    _check(_lib.moe_layer_decode(C.byref(layer.s), T, _dtype_code(x), _ptr(x), _ptr(h_res),
+                                 _ptr(h_out), _ptr(topk_idx), _ptr(topk_w), wp, wb,
+                                 _stream(stream)), "moe_layer_decode")
+
+
+def ws_view(layer: Layer, n_tokens: int, ws) -> dict:
+    """Views (fp32 tensors) of the intermediates moe_layer_decode leaves in ws."""
+    v = WsView()
+    _check(_lib.moe_layer_ws_view(C.byref(layer.s), n_tokens, _ptr(ws), ws.numel(), C.byref(v)),
+           "moe_layer_ws_view")
+    base = ws.data_ptr()
+    E, K, I = layer.n_experts, layer.top_k, layer.inter
+    f = ws.view(torch.uint8)
+
+    def sl(ptr, n):
+        o = ptr - base
+        return f[o:o + 4 * n].view(torch.float32)
+    return dict(logits=sl(v.logits, n_tokens * E).view(n_tokens, E),
+                sigma=sl(v.sigma, n_tokens),
+                h_routed=sl(v.h_routed, n_tokens * K * I).view(n_tokens, K, I),
+                h_shared=sl(v.h_shared, n_tokens * I).view(n_tokens, I))
+
+
+class Stack:
+    """Layers of one resident expert stack (all shaped like layers[0])."""
+
+    def __init__(self, layers: list[Layer]):
+        self.layers = layers
+        self.arr = (LayerStruct * len(layers))(*[l.s for l in layers])
+
+    def workspace(self) -> torch.Tensor:
+        n = int(_lib.moe_stack_workspace_bytes(C.byref(self.arr[0]), len(self.layers)))
+        return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+def stack_decode(stack: Stack, updates, h, idx_log, w_log, ws, stream=None):
+    _check(_lib.moe_stack_decode(stack.arr, len(stack.layers), _ptr(updates), _ptr(h),
+                                 _ptr(idx_log), _ptr(w_log), _ptr(ws), ws.numel(),
+                                 _stream(stream)), "moe_stack_decode")
+
+
+class Graph:
+    """An instantiated HIP graph (moe_graph_t)."""
+
+    def __init__(self, handle, keep=()):
+        self.h = handle
+        self.keep = keep  # tensors the graph's pointers refer to
+
+    def launch(self, stream=None):
+        _check(_lib.moe_graph_launch(self.h, _stream(stream)), "moe_graph_launch")
+
+    def destroy(self):
+        if self.h:
+            _check(_lib.moe_graph_destroy(self.h), "moe_graph_destroy")
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+
+def capture_begin(stream):
+    _check(_lib.moe_graph_capture_begin(stream.cuda_stream), "moe_graph_capture_begin")
+
+
+def capture_end(stream, keep=()) -> Graph:
+    h = C.c_void_p()
+    _check(_lib.moe_graph_capture_end(stream.cuda_stream, C.byref(h)), "moe_graph_capture_end")
+    return Graph(h, keep)
+
+
+def graph_stack(stack: Stack, updates, h, idx_log, w_log, ws, stream) -> Graph:
+    g = C.c_void_p()
+    _check(_lib.moe_graph_create_stack(stack.arr, len(stack.layers), _ptr(updates), _ptr(h),
+                                       _ptr(idx_log), _ptr(w_log), _ptr(ws), ws.numel(),
+                                       stream.cuda_stream, C.byref(g)), "moe_graph_create_stack")
+    return Graph(g, (stack, updates, h, idx_log, w_log, ws))
+
+
+def fill_experts(dst, stride: int, n: int, seed: int, layer: int, first_expert: int,
+                 hidden: int, inter: int, bits: int, dist, stream=None, offset: int = 0):
+    _check(_lib.moe_fill_experts(_ptr(dst) + offset, stride, n, seed, layer, first_expert,
+                                 hidden, inter, bits, dist.scale_lo, dist.scale_hi,
+                                 dist.bias_lo, dist.bias_hi, _stream(stream)),
+           "moe_fill_experts")
+
+
+def zero(t, stream=None):
+    _check(_lib.moe_zero(_ptr(t), t.numel() * t.element_size(), _stream(stream)), "moe_zero")

@@ -1,0 +1,248 @@
+/*
+ * moe.h -- C ABI of libmoe, the MI355X (gfx950) MoE expert hot path.
+ *
+ * One MoE layer for one token (or a micro-batch of tokens):
+ *   router matvec -> softmax -> top-K of E experts -> for the K routed experts
+ *   and one shared expert a groupwise-affine 4-bit or 2-bit dequantised matvec
+ *   (w = q * scale + bias) for gate and up, fused SwiGLU, the down matvec, and
+ *   a weighted combine with a sigmoid-gated shared expert plus the residual.
+ *
+ * The operations follow these pages (cited by site and section):
+ *   [openclawradar] openclawradar.com (ja), "Flash-MoE: running the 397B
+ *       parameter Qwen model on a MacBook Pro in pure C/Metal": "Technical
+ *       implementation" (hidden 4096, 512 experts, K=4 plus one shared),
+ *       "FMA-optimized dequant kernel", "Metal compute shaders" (4/2-bit
+ *       dequant matvec, fused SwiGLU, two-pass RMSNorm, combine + residual +
+ *       sigmoid gate), "Deferred GPU expert compute", "Pipeline performance"
+ *       (softmax + topK routing).
+ *   [a2a-fr] a2a-mcp.org (fr), "What is Flash-MoE?": "FMA-optimised
+ *       dequantisation kernels" (nibble * scale + bias).
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees, copies between host and device, or synchronises
+ *     in these calls, so every call may be captured into a HIP graph.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *   - Arguments are checked before anything is enqueued.  On failure the call
+ *     returns a negative status, enqueues nothing and leaves a message for
+ *     moe_last_error() (thread-local).  A failed kernel launch returns
+ *     MOE_EHIP with the HIP error string.  Faults inside kernels surface at the
+ *     caller's next stream synchronisation.
+ *   - Kernels never read outside the buffers described here.  An expert id
+ *     that is neither in [0, n_experts) nor MOE_SHARED yields a NaN row.
+ *   - Limits: bits 4 or 2, group 64 (else MOE_EUNSUPPORTED); hidden and inter
+ *     multiples of 64 in [64, 8192]; 1 <= top_k <= 8, top_k <= n_experts <=
+ *     1024; 1 <= n_tokens <= 64.  Alignment: records, expert_stride and the
+ *     workspace on 256 bytes, every other vector on 16 bytes (MOE_EALIGN).
+ *   - Reentrant: the only global state is the thread-local error string.
+ *
+ * Record format (one expert, `moe_expert_bytes` bytes, sections on 256-byte
+ * boundaries, in this order):
+ *   codes_gate [inter][hidden*bits/32] u32, codes_up [inter][hidden*bits/32],
+ *   codes_down [hidden][inter*bits/32], sb_gate [inter][hidden/64] u32,
+ *   sb_up [inter][hidden/64], sb_down [hidden][inter/64].
+ *   Codes are unsigned b-bit fields, little-endian in each 32-bit word: column
+ *   c of a row sits in word c*b/32 at bit b*(c mod 32/b).  Each sb word holds
+ *   the bf16 scale (low 16 bits) and bf16 bias (high 16 bits) of 64
+ *   consecutive input columns.  The dequantised weight is q*scale + bias with
+ *   no zero point ([a2a-fr] "FMA-optimised dequantisation kernels").
+ *   At hidden 4096 / inter 1024 / 4 bits a record is 7,077,888 bytes = 6.75
+ *   MiB, the "about 6.75 MB per expert" of [openclawradar] "SSD expert
+ *   streaming".
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* null pointer, bad size or count */
+    MOE_EUNSUPPORTED = -2,  /* bits, group or dtype outside what is built */
+    MOE_EALIGN = -3,        /* pointer or stride misaligned */
+    MOE_EWORKSPACE = -4,    /* workspace missing or too small */
+    MOE_EHIP = -5           /* a HIP runtime call failed */
+};
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* expert id that selects the layer's shared expert in an id list */
+#define MOE_SHARED (-1)
+
+/* One MoE layer: shapes, flags and device pointers to its weights.  A host
+ * struct, read by the callee only during the call. */
+typedef struct moe_layer {
+    int hidden;            /* H: model width */
+    int inter;             /* I: expert intermediate width (routed and shared) */
+    int n_experts;         /* E: routed experts */
+    int top_k;             /* K: routed experts per token */
+    int group;             /* quantisation group along the input dim; must be 64 */
+    int bits_routed;       /* 4 or 2 */
+    int bits_shared;       /* 4 or 2 */
+    int renorm_topk;       /* 1: the K selected probabilities are divided by
+                              their sum; 0: they are the plain softmax values */
+    moe_dtype router_dtype;
+    const void *router;    /* [E][H] router weights, expert-major */
+    moe_dtype gate_dtype;
+    const void *shared_gate;   /* [H] shared-expert gate vector g */
+    const void *experts;       /* E routed records, `expert_stride` bytes apart */
+    size_t expert_stride;
+    const void *shared_expert; /* one record at bits_shared */
+} moe_layer_t;
+
+/* ---------------------------------------------------------------------- */
+/* status, sizes                                                           */
+/* ---------------------------------------------------------------------- */
+const char *moe_strerror(int status);
+/* Detail of the last failure on this thread ("" if none). */
+const char *moe_last_error(void);
+/* ABI version of this header (increments on incompatible change). */
+int moe_abi_version(void);
+
+/* Bytes of one quantised [rows][cols] matrix: codes plus sb words, each
+ * section rounded up to 256 bytes.  0 when the shape is invalid. */
+size_t moe_qmatrix_bytes(int rows, int cols, int bits, int group);
+/* Bytes of one expert record (see the format above).  0 when invalid. */
+size_t moe_expert_bytes(int hidden, int inter, int bits, int group);
+/* Byte offsets of the six sections of a record, in record order:
+ * codes_gate, codes_up, codes_down, sb_gate, sb_up, sb_down. */
+int moe_expert_offsets(int hidden, int inter, int bits, int group, size_t out[6]);
+/* Workspace bytes that moe_layer_decode / moe_route / moe_expert_forward_*
+ * need for this layer and token count (0 if the layer is invalid). */
+size_t moe_layer_workspace_bytes(const moe_layer_t *L, int n_tokens);
+/* Workspace bytes moe_stack_decode needs for `n_layers` layers shaped like L. */
+size_t moe_stack_workspace_bytes(const moe_layer_t *L, int n_layers);
+
+/* ---------------------------------------------------------------------- */
+/* the path, stage by stage                                                 */
+/* ---------------------------------------------------------------------- */
+/* Router matvec, softmax, top-K and the shared sigmoid gate for n_tokens
+ * tokens ([openclawradar] "Pipeline performance": routing, then softmax +
+ * topK).
+ *   x            [n_tokens][H], x_dtype
+ *   topk_idx     [n_tokens][K] int32: the K largest logits, exact ties to the
+ *                lower expert index, in descending order
+ *   topk_w       [n_tokens][K] fp32: softmax probabilities of those experts
+ *                (renormalised to sum 1 when L->renorm_topk)
+ *   shared_sigma [n_tokens] fp32: 1 / (1 + exp(-(g . x)))
+ *   logits       [n_tokens][E] fp32, or NULL
+ *   ws           workspace of moe_layer_workspace_bytes(L, n_tokens) bytes */
+int moe_route(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void *x,
+              int32_t *topk_idx, float *topk_w, float *shared_sigma, float *logits,
+              void *ws, size_t ws_bytes, void *stream);
+
+/* Expert forward for a list of experts on one token: for each listed id e,
+ *   h_e = silu(W_gate(e) x) * (W_up(e) x)   [I]   (fused SwiGLU)
+ *   y_e = W_down(e) h_e                      [H]
+ * with every W the dequantised q*scale + bias matrix ([openclawradar]
+ * "FMA-optimized dequant kernel", "Metal compute shaders").
+ *   expert_ids  [n] int32 device array; MOE_SHARED selects the shared record
+ *   y           [n][H] fp32 output
+ *   h           [n][I] fp32 output, or NULL (then kept in the workspace)
+ * The _q4 entry point needs L->bits_routed == 4, the _q2 entry point
+ * L->bits_routed == 2; a MOE_SHARED entry whose bits_shared differs from the
+ * entry point's width yields a NaN row.  1 <= n <= 64. */
+int moe_expert_forward_q4(const moe_layer_t *L, moe_dtype x_dtype, const void *x,
+                          const int32_t *expert_ids, int n, float *y, float *h,
+                          void *ws, size_t ws_bytes, void *stream);
+int moe_expert_forward_q2(const moe_layer_t *L, moe_dtype x_dtype, const void *x,
+                          const int32_t *expert_ids, int n, float *y, float *h,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* out[o] = h_res[o] + sum_k w[k] * y[k][o] + shared_sigma[0] * y_shared[o]
+ * ([openclawradar] "Metal compute shaders": MoE combine + residual + sigmoid
+ * gate in one pass).  y is [n_routed][hidden]; every array fp32.  h_out may
+ * alias h_res. */
+int moe_combine(int hidden, int n_routed, const float *h_res, const float *y,
+                const float *w, const float *y_shared, const float *shared_sigma,
+                float *h_out, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* whole layer, whole stack                                                 */
+/* ---------------------------------------------------------------------- */
+/* One MoE layer for n_tokens tokens with no host round trip: routing, the K
+ * routed experts and the shared expert, combine + residual.
+ *   x        [n_tokens][H] (x_dtype), the normalised activation
+ *   h_res    [n_tokens][H] fp32 residual; h_out [n_tokens][H] fp32 (may not
+ *            alias h_res)
+ *   topk_idx [n_tokens][K], topk_w [n_tokens][K]: the routing decision
+ * Intermediates (logits, sigma, h_e, the shared expert's y) stay in `ws`; see
+ * moe_layer_ws_view. */
+int moe_layer_decode(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void *x,
+                     const float *h_res, float *h_out, int32_t *topk_idx, float *topk_w,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Device pointers of the intermediates moe_layer_decode leaves in ws. */
+typedef struct moe_ws_view {
+    float *logits;       /* [n_tokens][E] */
+    float *sigma;        /* [n_tokens] */
+    float *h_routed;     /* [n_tokens][K][I] routed SwiGLU outputs, idx order */
+    float *h_shared;     /* [n_tokens][I] shared SwiGLU output */
+} moe_ws_view;
+int moe_layer_ws_view(const moe_layer_t *L, int n_tokens, void *ws, size_t ws_bytes,
+                      moe_ws_view *view);
+
+/* One token through n_layers layers, residual carried in fp32:
+ *   for l: h <- h + u_l (u_l = updates_bf16[l], skipped when NULL);
+ *          x = h / sqrt(mean(h^2) + 1e-6)  (two-pass RMSNorm, unit weight,
+ *          [openclawradar] "Metal compute shaders");
+ *          h <- h + MoE_l(x)   (moe_layer_decode with h_res = h)
+ *   h       [H] fp32, read and overwritten
+ *   idx_log [n_layers][K], w_log [n_layers][K]: routing of every layer
+ * All layers must share hidden/inter/E/K/bits/dtypes with layers[0]. */
+int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *updates_bf16,
+                     float *h, int32_t *idx_log, float *w_log,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* HIP graphs ([openclawradar] "Deferred GPU expert compute": the expert     */
+/* pass is queued without a host wait)                                      */
+/* ---------------------------------------------------------------------- */
+typedef struct moe_graph_s *moe_graph_t;
+/* Start capturing every call made on `stream` (which must not be the NULL
+ * stream) into a graph; end and instantiate it with moe_graph_capture_end. */
+int moe_graph_capture_begin(void *stream);
+int moe_graph_capture_end(void *stream, moe_graph_t *out);
+/* Capture moe_stack_decode with these arguments (the buffers must outlive
+ * the graph). */
+int moe_graph_create_stack(const moe_layer_t *layers, int n_layers,
+                           const uint16_t *updates_bf16, float *h, int32_t *idx_log,
+                           float *w_log, void *ws, size_t ws_bytes, void *stream,
+                           moe_graph_t *out);
+int moe_graph_launch(moe_graph_t g, void *stream);
+int moe_graph_destroy(moe_graph_t g);
+
+/* ---------------------------------------------------------------------- */
+/* synthetic weights                                                        */
+/* ---------------------------------------------------------------------- */
+/* Fill n expert records at dst (stride bytes apart) with seeded synthetic
+ * weights: codes uniform over 0..2^bits-1 and (scale, bias) uniform in
+ * [scale_lo, scale_hi) x [bias_lo, bias_hi), rounded to bf16.  Record j gets
+ * generator ids (seed, layer, first_expert + j).  The numbers come from the
+ * SplitMix64 generator (Steele, Lea and Flood, OOPSLA 2014) used
+ * counter-style: output i of a generator in state k is mix(k + (i+1)*GAMMA);
+ * key(seed, layer, expert, section) applies that rule once per id starting
+ * from the root state 0x6D6F652D67656E31.  Code words: output j fills words
+ * 2j (low half) and 2j+1 (high half).  sb word i: output i, scale from its
+ * bits 40..63 and bias from bits 16..39 as v = lo + (hi-lo)*((u+0.5)/2^24) in
+ * fp64 without contraction, then rounded to nearest-even bf16.
+ * Sections 0..5 are codes_gate, codes_up, codes_down, sb_gate, sb_up,
+ * sb_down.  Padding bytes are left untouched. */
+int moe_fill_experts(void *dst, size_t stride, int n, uint64_t seed, int layer,
+                     int first_expert, int hidden, int inter, int bits,
+                     double scale_lo, double scale_hi, double bias_lo, double bias_hi,
+                     void *stream);
+
+/* Zero `bytes` bytes at `ptr` with a kernel (no memset node, safe inside a
+ * captured graph).  ptr 16-byte aligned. */
+int moe_zero(void *ptr, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */
