@@ -14,13 +14,11 @@
 // fma(q*x, scale, bias*x)).  All are regroupings of one sum.  Here the sum is
 // regrouped per 64-column group g (one scale s_g and bias b_g):
 //     y = sum_g s_g * (sum_{c in g} q_c x_c) + b_g * (sum_{c in g} x_c)
-// and the inner integer-weighted sums run on the packed bf16 dot instruction
-// (v_dot2_f32_bf16, products exact in fp32): a code q becomes the bf16 number
-// 128 + q * 2^k by OR-ing it into the mantissa of 128.0, the matching x is
-// pre-scaled by 2^-k, and the constant 128 * x' part is subtracted through the
-// accumulator's start value.  x is staged once per lane (every lane always
-// sees the same input columns), as bf16 pairs, or as hi + lo bf16 pairs when
-// the input is fp32 (16 significant bits).
+// where the integer-weighted inner sums carry exact products: on the packed
+// bf16 dot instruction (v_dot2_f32_bf16) when x is bf16, with codes made into
+// bf16 numbers by OR-ing them into a mantissa; in fp32 FMAs after the byte
+// converts when x is fp32.  x is staged once per lane (a lane always sees the
+// same input columns) and the bias term needs only the chunk sums of x.
 //
 // Memory mapping: a wave reads whole quantised rows with 128-bit loads, lane l
 // taking 16-byte chunks l, l+64, ... of a row (rows shorter than 64 chunks are
@@ -36,8 +34,6 @@ namespace moe_impl {
 // ---------------------------------------------------------------------------
 // small helpers
 // ---------------------------------------------------------------------------
-constexpr uint32_t kMagic2 = 0x43004300u;  // two bf16 128.0
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
@@ -78,43 +74,54 @@ __device__ __forceinline__ float seg_sum(float v, int lg) {
 __device__ __forceinline__ float silu_mul(float a, float u) { return a / (1.0f + expf(-a)) * u; }
 
 // ---------------------------------------------------------------------------
-// staged input chunk: the bf16 pairs that meet one 16-byte code chunk
+// staged input chunk: what one lane keeps of x for one 16-byte code chunk
 // ---------------------------------------------------------------------------
-// 4-bit chunk = 32 columns = 4 words; word t holds columns 8t..8t+7, nibble
-//   k of each 16-bit half is column 8t+k (low half) / 8t+4+k (high half).
-//   Pair 4t+k is (x[8t+k], x[8t+4+k]) at scale 1.
-// 2-bit chunk = 64 columns = 4 words; word t holds columns 16t..16t+15, field
-//   j of each half is column 16t+j / 16t+8+j.  Pair 8t+j is (x[16t+j],
-//   x[16t+8+j]) pre-scaled by 2^-k_j with k_j = {0,2,4,0,2,4,0,2}[j]: the
-//   field is OR-ed into the mantissa at bit k_j.
+// A 4-bit chunk covers 32 columns in 4 words: word t holds columns 8t..8t+7,
+// column 8t+n at bits 4n.  A 2-bit chunk covers 64 columns: word t holds
+// columns 16t..16t+15, column 16t+f at bits 2f.
+//
+// bf16 input (XF32 = false): the dot runs on v_dot2_f32_bf16.  A code is
+//   moved to mantissa bits 3..6 of bf16 16.0 (0x4180), which makes the bf16
+//   number 16 + q (a 2-bit field at bits 5..6 gives 16 + 4q, met by x/4).
+//   Products are exact in fp32; the constant 16 * x part ("off", computed at
+//   staging with the same instruction) is removed through the accumulator's
+//   start value.  With the code at the top of the mantissa the constant part
+//   stays small next to q * x, so little precision is lost to cancellation.
+//   4-bit pair 4t+n = (x[8t+n], x[8t+4+n]): nibble n of each 16-bit half.
+//   2-bit pair 8t+f = (x[16t+f], x[16t+8+f]) * (f odd ? 1/4 : 1).
+// fp32 input (XF32 = true): codes become fp32 through the byte converts
+//   (v_cvt_f32_ubyte0..3 of nibble- or field-masked words) and meet x in fp32
+//   FMAs, so nothing of x is rounded.
 template <int BITS>
 struct ChunkGeom {
   static constexpr int kCols = 128 / BITS;        // columns per 16-byte chunk
   static constexpr int kPairs = kCols / 2;
 };
 
-template <int BITS, bool HILO>
-struct XStage {
-  uint32_t hi[ChunkGeom<BITS>::kPairs];
-  uint32_t lo[HILO ? ChunkGeom<BITS>::kPairs : 1];
-  float off;  // what the 128.0 part of the codes contributes to the dot
+constexpr uint32_t kMagic16 = 0x41804180u;  // two bf16 16.0
+
+template <int BITS, bool XF32>
+struct XStage;
+
+template <int BITS>
+struct XStage<BITS, false> {
+  uint32_t p[ChunkGeom<BITS>::kPairs];
+  float off;  // sum over the chunk of 16 * x' (the constant part of the codes)
   float xs;   // sum of x over the chunk (multiplies the group bias)
 };
 
 template <int BITS>
-__device__ __forceinline__ float pair_scale(int j) {
-  if constexpr (BITS == 4) {
-    return 1.0f;
-  } else {
-    const int k = (j % 3) * 2;  // 0,2,4,0,2,4,0,2
-    return k == 0 ? 1.0f : (k == 2 ? 0.25f : 0.0625f);
-  }
-}
+struct XStage<BITS, true> {
+  float v[ChunkGeom<BITS>::kCols];
+  float xs;
+};
 
-template <int BITS, bool HILO>
+template <int BITS>
 __device__ __forceinline__ void stage_chunk(const float (&v)[ChunkGeom<BITS>::kCols],
-                                            XStage<BITS, HILO> &s) {
+                                            XStage<BITS, false> &s) {
   constexpr int NC = ChunkGeom<BITS>::kCols;
+  constexpr int CPW = NC / 4;                        // columns per word
+  constexpr int PPW = ChunkGeom<BITS>::kPairs / 4;   // pairs per word
   float xs = 0.f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) xs += v[c];
@@ -122,67 +129,115 @@ __device__ __forceinline__ void stage_chunk(const float (&v)[ChunkGeom<BITS>::kC
   float off = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    constexpr int PPW = ChunkGeom<BITS>::kPairs / 4;  // pairs per word
-    constexpr int CPW = NC / 4;                        // columns per word
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
-      const float sc = pair_scale<BITS>(j);
-      const float a = v[CPW * t + j] * sc;
-      const float b = v[CPW * t + CPW / 2 + j] * sc;
-      const uint32_t ha = bf16_rne(a), hb = bf16_rne(b);
+      const float sc = (BITS == 2 && (j & 1)) ? 0.25f : 1.0f;
+      const uint32_t ha = bf16_rne(v[CPW * t + j] * sc);
+      const uint32_t hb = bf16_rne(v[CPW * t + CPW / 2 + j] * sc);
       const uint32_t hp = ha | (hb << 16);
-      s.hi[PPW * t + j] = hp;
-      off = dot2bf(kMagic2, hp, off);
-      if constexpr (HILO) {
-        const uint32_t la = bf16_rne(a - __uint_as_float(ha << 16));
-        const uint32_t lb = bf16_rne(b - __uint_as_float(hb << 16));
-        const uint32_t lp = la | (lb << 16);
-        s.lo[PPW * t + j] = lp;
-        off = dot2bf(kMagic2, lp, off);
-      }
+      s.p[PPW * t + j] = hp;
+      off = dot2bf(kMagic16, hp, off);
     }
   }
   s.off = off;
 }
 
+template <int BITS>
+__device__ __forceinline__ void stage_chunk(const float (&v)[ChunkGeom<BITS>::kCols],
+                                            XStage<BITS, true> &s) {
+  constexpr int NC = ChunkGeom<BITS>::kCols;
+  float xs = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    s.v[c] = v[c];
+    xs += v[c];
+  }
+  s.xs = xs;
+}
+
+// hide a value's provenance so that the byte-select converts are formed
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // sum_c q_c * x_c over one 16-byte code chunk
-template <int BITS, bool HILO>
-__device__ __forceinline__ float chunk_dot(const uint4 &q, const XStage<BITS, HILO> &s) {
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(const uint4 &q, const XStage<BITS, false> &s,
+                                           uint32_t kMagic16) {
   float acc = -s.off;
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
+    const uint32_t a = w[t] << 3, b = w[t] >> 1, c = w[t] >> 5, d = w[t] >> 9;
     if constexpr (BITS == 4) {
-      const uint32_t p0 = (w[t] & 0x000F000Fu) | kMagic2;
-      const uint32_t p1 = ((w[t] >> 4) & 0x000F000Fu) | kMagic2;
-      const uint32_t p2 = ((w[t] >> 8) & 0x000F000Fu) | kMagic2;
-      const uint32_t p3 = ((w[t] >> 12) & 0x000F000Fu) | kMagic2;
-      acc = dot2bf(p0, s.hi[4 * t + 0], acc);
-      acc = dot2bf(p1, s.hi[4 * t + 1], acc);
-      acc = dot2bf(p2, s.hi[4 * t + 2], acc);
-      acc = dot2bf(p3, s.hi[4 * t + 3], acc);
-      if constexpr (HILO) {
-        acc = dot2bf(p0, s.lo[4 * t + 0], acc);
-        acc = dot2bf(p1, s.lo[4 * t + 1], acc);
-        acc = dot2bf(p2, s.lo[4 * t + 2], acc);
-        acc = dot2bf(p3, s.lo[4 * t + 3], acc);
-      }
+      acc = dot2bf((a & 0x00780078u) | kMagic16, s.p[4 * t + 0], acc);
+      acc = dot2bf((b & 0x00780078u) | kMagic16, s.p[4 * t + 1], acc);
+      acc = dot2bf((c & 0x00780078u) | kMagic16, s.p[4 * t + 2], acc);
+      acc = dot2bf((d & 0x00780078u) | kMagic16, s.p[4 * t + 3], acc);
     } else {
-      const uint32_t w6 = w[t] >> 6, w12 = w[t] >> 12;
-      const uint32_t p[8] = {
-          (w[t] & 0x00030003u) | kMagic2, (w[t] & 0x000C000Cu) | kMagic2,
-          (w[t] & 0x00300030u) | kMagic2, (w6 & 0x00030003u) | kMagic2,
-          (w6 & 0x000C000Cu) | kMagic2,   (w6 & 0x00300030u) | kMagic2,
-          (w12 & 0x00030003u) | kMagic2,  (w12 & 0x000C000Cu) | kMagic2};
+      acc = dot2bf((a & 0x00180018u) | kMagic16, s.p[8 * t + 0], acc);
+      acc = dot2bf((a & 0x00600060u) | kMagic16, s.p[8 * t + 1], acc);
+      acc = dot2bf((b & 0x00180018u) | kMagic16, s.p[8 * t + 2], acc);
+      acc = dot2bf((b & 0x00600060u) | kMagic16, s.p[8 * t + 3], acc);
+      acc = dot2bf((c & 0x00180018u) | kMagic16, s.p[8 * t + 4], acc);
+      acc = dot2bf((c & 0x00600060u) | kMagic16, s.p[8 * t + 5], acc);
+      acc = dot2bf((d & 0x00180018u) | kMagic16, s.p[8 * t + 6], acc);
+      acc = dot2bf((d & 0x00600060u) | kMagic16, s.p[8 * t + 7], acc);
+    }
+  }
+  return acc;
+}
+
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(const uint4 &q, const XStage<BITS, true> &s) {
+  float acc = 0.f;
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc = dot2bf(p[j], s.hi[8 * t + j], acc);
-      if constexpr (HILO) {
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (BITS == 4) {
+      // bytes of lo: nibbles 0,2,4,6; bytes of hi: nibbles 1,3,5,7
+      const uint32_t lo = opaque(w[t] & 0x0F0F0F0Fu);
+      const uint32_t hi = opaque((w[t] >> 4) & 0x0F0F0F0Fu);
+      const float *x = s.v + 8 * t;
+      acc = fmaf((float)(lo & 0xFFu), x[0], acc);
+      acc = fmaf((float)(hi & 0xFFu), x[1], acc);
+      acc = fmaf((float)((lo >> 8) & 0xFFu), x[2], acc);
+      acc = fmaf((float)((hi >> 8) & 0xFFu), x[3], acc);
+      acc = fmaf((float)((lo >> 16) & 0xFFu), x[4], acc);
+      acc = fmaf((float)((hi >> 16) & 0xFFu), x[5], acc);
+      acc = fmaf((float)(lo >> 24), x[6], acc);
+      acc = fmaf((float)(hi >> 24), x[7], acc);
+    } else {
+      // byte b of f_k is field 4b + k
+      const uint32_t f0 = opaque(w[t] & 0x03030303u);
+      const uint32_t f1 = opaque((w[t] >> 2) & 0x03030303u);
+      const uint32_t f2 = opaque((w[t] >> 4) & 0x03030303u);
+      const uint32_t f3 = opaque((w[t] >> 6) & 0x03030303u);
+      const float *x = s.v + 16 * t;
+      const uint32_t f[4] = {f0, f1, f2, f3};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc = dot2bf(p[j], s.lo[8 * t + j], acc);
+      for (int bb = 0; bb < 4; ++bb) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t byte = bb == 3 ? (f[k] >> 24) : ((f[k] >> (8 * bb)) & 0xFFu);
+          acc = fmaf((float)byte, x[4 * bb + k], acc);
+        }
       }
     }
   }
   return acc;
+}
+
+template <int BITS>
+__device__ __forceinline__ float chunk_dot_any(const uint4 &q, const XStage<BITS, false> &s,
+                                               uint32_t magic) {
+  return chunk_dot<BITS>(q, s, magic);
+}
+template <int BITS>
+__device__ __forceinline__ float chunk_dot_any(const uint4 &q, const XStage<BITS, true> &s,
+                                               uint32_t) {
+  return chunk_dot<BITS>(q, s);
 }
 
 // load the x values of one chunk (columns col0 .. col0 + kCols - 1) as fp32
@@ -254,7 +309,7 @@ template <int BITS, int NCH, int NPASS, int XS>
 __device__ __forceinline__ void gateup_wave(const uint8_t *rec, const RecOffsets &off,
                                             int H, int I, int row0, bool valid,
                                             const void *x, const float *xl, float *h_out) {
-  constexpr bool HILO = (XS != XS_BF16);
+  constexpr bool XF32 = (XS != XS_BF16);
   const RowMap m = row_map<BITS>(H);
   const uint32_t *gc = reinterpret_cast<const uint32_t *>(rec + off.gate_codes);
   const uint32_t *uc = reinterpret_cast<const uint32_t *>(rec + off.up_codes);
@@ -285,17 +340,20 @@ __device__ __forceinline__ void gateup_wave(const uint8_t *rec, const RecOffsets
     }
   }
 
-  XStage<BITS, HILO> xs[NCH];
+  XStage<BITS, XF32> xs[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = m.li + (j << m.lg);
     if (c < m.cpr) {
       float v[ChunkGeom<BITS>::kCols];
       load_x_chunk<BITS, XS>(x, xl, c * ChunkGeom<BITS>::kCols, v);
-      stage_chunk<BITS, HILO>(v, xs[j]);
+      stage_chunk<BITS>(v, xs[j]);
     }
   }
 
+  // the magic constant lives in a VGPR so that mask-and-or is one v_and_or_b32
+  // (gfx9 VOP3 reads at most one scalar or literal operand)
+  const uint32_t magic = opaque(kMagic16);
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) {
     float a = 0.f, u = 0.f;
@@ -303,8 +361,8 @@ __device__ __forceinline__ void gateup_wave(const uint8_t *rec, const RecOffsets
     for (int j = 0; j < NCH; ++j) {
       const int c = m.li + (j << m.lg);
       if (c < m.cpr) {
-        const float da = chunk_dot<BITS, HILO>(gq[p][j], xs[j]);
-        const float du = chunk_dot<BITS, HILO>(uq[p][j], xs[j]);
+        const float da = chunk_dot_any<BITS>(gq[p][j], xs[j], magic);
+        const float du = chunk_dot_any<BITS>(uq[p][j], xs[j], magic);
         a = fmaf(bf_lo(gsw[p][j]), da, fmaf(bf_hi(gsw[p][j]), xs[j].xs, a));
         u = fmaf(bf_lo(usw[p][j]), du, fmaf(bf_hi(usw[p][j]), xs[j].xs, u));
       }
@@ -624,7 +682,7 @@ __device__ __forceinline__ void down_accumulate(const float *hin, const RowMap &
     if (c < m.cpr) {
       float v[ChunkGeom<BITS>::kCols];
       load_x_chunk<BITS, XS_F32>(hin, nullptr, c * ChunkGeom<BITS>::kCols, v);
-      stage_chunk<BITS, true>(v, xs[j]);
+      stage_chunk<BITS>(v, xs[j]);
     }
   }
 #pragma unroll
@@ -634,7 +692,7 @@ __device__ __forceinline__ void down_accumulate(const float *hin, const RowMap &
     for (int j = 0; j < NCH; ++j) {
       const int c = m.li + (j << m.lg);
       if (c < m.cpr) {
-        const float d = chunk_dot<BITS, true>(q[p][j], xs[j]);
+        const float d = chunk_dot<BITS>(q[p][j], xs[j]);
         part = fmaf(bf_lo(sb[p][j]), d, fmaf(bf_hi(sb[p][j]), xs[j].xs, part));
       }
     }
