@@ -1,0 +1,259 @@
+"""Benchmark of the MoE expert hot path on one MI355X.
+
+Workload (N=1): the Qwen3.5-397B-A17B-shaped MoE layer decode at batch 1 --
+hidden 4096, expert intermediate 1024, 512 routed experts, top-4 plus one
+sigmoid-gated shared expert, 4-bit groupwise-affine experts (group 64, bf16
+scale/bias), bf16 router and x.  Synthetic weights and inputs (seeded).
+
+A step is one replay of a HIP graph that holds R = 128 independent layer
+decodes (a rotation set: distinct router, shared-gate vector, shared expert and
+activation per instance over one 512-expert pool, 5 GB touched per replay), so
+that no layer's weights are still in the 256 MB Infinity Cache when it runs.
+`value` is the decode latency of one layer = step time / R.
+
+Also reported: per-kernel durations measured with HIP events around each launch
+(the library's timing hook), the roofline of the dominant kernel (routed
+gate/up), and the fp64 CPU oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer decode latency (us) and effective HBM GB/s (% of peak), 4-bit, batch 1"
+PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--instances", type=int, default=128)
+    ap.add_argument("--workload", default="q4_layer", choices=["q4_layer", "q2_layer"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--profile-passes", type=int, default=3)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (counter scaling for rocprofv3 --pmc)")
+    return ap.parse_args()
+
+
+def kernel_bytes(cfg):
+    """Algorithmic bytes per launch of each kernel of one layer decode."""
+    from bit_dequant_expert_route_amd import synth
+    H, I, E, K = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
+
+    def mat(rows, cols, bits):
+        return rows * cols * bits // 8 + rows * (cols // 64) * 4
+    xb = H * (2 if cfg.x_dtype == "bf16" else 4)
+    rb = 2 if cfg.router_dtype == "bf16" else 4
+    # the shared expert's gate/up runs with the routed gate/up when both have
+    # the same width, otherwise with the router
+    shared_gu = 2 * mat(I, H, cfg.bits_shared) + I * 4
+    same = cfg.bits_shared == cfg.bits_routed
+    head = E * H * rb + H * rb + xb + E * 4 + 4 + (0 if same else shared_gu)
+    gateup = K * 2 * mat(I, H, cfg.bits_routed) + xb + E * 4 + K * I * 4 + K * 8 + (shared_gu if same else 0)
+    down = (K * mat(H, I, cfg.bits_routed) + mat(H, I, cfg.bits_shared) + K * I * 4 + I * 4
+            + 2 * H * 4 + K * 8 + 4)
+    weights = cfg.weight_bytes_per_token_layer()
+    assert weights == E * H * rb + H * rb + K * synth.record_layout(H, I, cfg.bits_routed).total \
+        + synth.record_layout(H, I, cfg.bits_shared).total
+    return dict(head=head, gateup=gateup, down_combine=down, layer_weights=weights,
+                layer_total=head + gateup + down)
+
+
+def source_sha():
+    h = hashlib.sha256()
+    for f in ("moe_kernels.hip", "moe_api.cpp", "moe_internal.h"):
+        h.update(open(os.path.join(ROOT, "bit_dequant_expert_route_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_sha") != source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def build_rotation(cfg, R, seed0=1000):
+    import torch
+    from bit_dequant_expert_route_amd import moe, synth
+    H, I, E = cfg.hidden, cfg.inter, cfg.n_experts
+    rb = synth.record_layout(H, I, cfg.bits_routed).total
+    sb = synth.record_layout(H, I, cfg.bits_shared).total
+    pool = torch.empty(E * rb, dtype=torch.uint8, device="cuda")
+    moe.fill_experts(pool, rb, E, seed0, 0, 0, H, I, cfg.bits_routed,
+                     synth.dist_for_bits(cfg.bits_routed))
+    shared = torch.empty(R * sb, dtype=torch.uint8, device="cuda")
+    moe.fill_experts(shared, sb, R, seed0, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared,
+                     synth.dist_for_bits(cfg.bits_shared))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed0)
+    layers, xs, hres = [], [], []
+    for i in range(R):
+        router = (torch.randn(E, H, generator=g, device="cuda") * synth.ROUTER_STD).to(torch.bfloat16)
+        gate = (torch.randn(H, generator=g, device="cuda") * synth.GATEVEC_STD).to(torch.bfloat16)
+        h = torch.randn(H, generator=g, device="cuda")
+        x = (h / torch.sqrt(torch.mean(h * h) + 1e-6)).to(torch.bfloat16)
+        layers.append(moe.Layer(hidden=H, inter=I, n_experts=E, top_k=cfg.top_k,
+                                bits_routed=cfg.bits_routed, bits_shared=cfg.bits_shared,
+                                renorm=True, router=router, gate_vec=gate, experts=pool,
+                                expert_stride=rb, shared_expert=shared[i * sb:(i + 1) * sb]))
+        xs.append(x)
+        hres.append(h)
+    torch.cuda.synchronize()
+    return layers, xs, hres, pool, shared
+
+
+def cpu_baseline(cfg, budget_s):
+    """fp64 oracle on the host: route + K routed experts + shared + combine for
+    as many sampled layer instances as fit the time budget."""
+    import oracle
+    from bit_dequant_expert_route_amd import synth
+    orc = oracle.get()
+    H, I = cfg.hidden, cfg.inter
+    times = []
+    t_end = time.perf_counter() + budget_s
+    i = 0
+    while time.perf_counter() < t_end or i == 0:
+        seed = 5000 + i
+        router = synth.router_weights(cfg, seed)
+        gate = synth.shared_gate_vector(cfg, seed)
+        h_res = synth.residual(cfg, seed)
+        x64 = orc.rmsnorm(h_res.astype(np.float64))
+        xb = synth.bf16_to_f32(synth.f64_to_bf16_rne(x64)).astype(np.float64)
+        # weight generation is excluded from the timed region
+        logits = orc.router(router, cfg.router_dtype, xb)
+        idx = orc.topk(logits, cfg.top_k)
+        recs = [synth.make_record(seed, 0, int(e), H, I, cfg.bits_routed) for e in idx]
+        shared = synth.make_record(seed, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared)
+        t0 = time.perf_counter()
+        r = orc.route(router, cfg.router_dtype, gate, cfg.gate_dtype, xb, cfg.top_k, True)
+        ys = [orc.expert(rec, H, I, cfg.bits_routed, xb)[1] for rec in recs]
+        ysh = orc.expert(shared, H, I, cfg.bits_shared, xb)[1]
+        orc.combine(h_res.astype(np.float64), np.stack(ys), r["w"], ysh, r["sigma"])
+        times.append(time.perf_counter() - t0)
+        i += 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return dict(value=float(np.median(times) * 1e6), unit="us", cores=threads, kind="oracle",
+                sample=f"{len(times)} single-token layer decodes of the {cfg.name} workload "
+                       f"(fp64 oracle, OpenMP over output rows, weight generation excluded), median")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the hot path is a single-GPU "
+                                   "kernel sequence with no sharding or collectives; run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+    from bit_dequant_expert_route_amd import moe, synth
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": a.numel(), "dispatches": 3}))
+        return
+
+    cfg = synth.CONFIGS[args.workload]
+    R = args.instances
+    kb = kernel_bytes(cfg)
+    layers, xs, hres, pool, shared = build_rotation(cfg, R)
+    K = cfg.top_k
+    out = torch.empty(cfg.hidden, device="cuda")
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    w = torch.empty(K, device="cuda")
+    ws = layers[0].workspace(1)
+
+    def one_pass(stream=None):
+        for i in range(R):
+            moe.layer_decode(layers[i], xs[i], hres[i], out, idx, w, ws, stream=stream)
+
+    one_pass()
+    torch.cuda.synchronize()
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        moe.capture_begin(s)
+        one_pass(s)
+        graph = moe.capture_end(s, keep=(layers, xs, hres, out, idx, w, ws))
+    for _ in range(args.warmup):
+        graph.launch(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(args.steps):
+        graph.launch(s)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    us_per_layer = ms_per_step * 1000.0 / R
+
+    # per-kernel durations (HIP events around each launch, eager launches)
+    n_launch = args.profile_passes * R * 4
+    moe.profile_begin(n_launch)
+    for _ in range(args.profile_passes):
+        one_pass()
+    rec = moe.profile_end(n_launch)
+    per = {}
+    for name, ms in rec:
+        per.setdefault(name, []).append(ms)
+    kern_us = {k: float(np.mean(v) * 1000.0) for k, v in per.items()}
+    dom = "gateup"
+    achieved = kb[dom] / (kern_us[dom] * 1e-6) / 1e9
+    traffic = traffic_from_profiles(args.workload, dom)
+
+    line = {
+        "metric": METRIC,
+        "value": round(us_per_layer, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: MoE layer decode, batch 1, hidden {cfg.hidden}, "
+                               f"expert intermediate {cfg.inter}, {cfg.n_experts} experts, "
+                               f"top-{K} + 1 shared, {cfg.bits_routed}-bit experts (group 64, bf16 "
+                               f"scale/bias), bf16 router and x",
+                   "layer_instances_per_step": R, "hbm_bytes_per_layer": kb["layer_total"]},
+        "effective_GBps": round(kb["layer_total"] / (us_per_layer * 1e-6) / 1e9, 1),
+        "pct_hbm_peak": round(100.0 * kb["layer_total"] / (us_per_layer * 1e-6) / 1e9 / PEAK_GBPS, 2),
+        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "roofline": {"bound": "hbm", "kernel": "k_gateup (shared + routed gate/up + SwiGLU)",
+                     "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+                     "bytes_per_launch": kb[dom]},
+        "cpu_baseline": None,
+    }
+    del graph
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

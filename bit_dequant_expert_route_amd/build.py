@@ -11,7 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = [os.path.join(CSRC, "moe_kernels.hip"), os.path.join(CSRC, "moe_api.cpp")]
+SOURCES = [os.path.join(CSRC, "moe_kernels.hip"), os.path.join(CSRC, "moe_util.hip"),
+           os.path.join(CSRC, "moe_api.cpp")]
 HEADERS = [os.path.join(CSRC, "moe_internal.h"),
            os.path.join(os.path.dirname(HERE), "include", "moe.h")]
 

@@ -15,6 +15,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "../../include/moe.h"
 #include "moe_internal.h"
 
@@ -36,6 +38,38 @@ int hip_fail(hipError_t e, const char *what) {
   return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// kernel timing state of this thread (moe_profile_begin / moe_profile_end)
+struct Prof {
+  bool on = false;
+  int cap = 0, n = 0;
+  std::vector<hipEvent_t> ev;  // two per launch
+  std::vector<int> ids;
+};
+thread_local Prof g_prof;
+
+bool prof_active(hipStream_t s) {
+  if (!g_prof.on || g_prof.n >= g_prof.cap) return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
+  return true;
+}
+
+// launch `fn` with events around it when profiling
+template <class F>
+hipError_t timed(hipStream_t s, int id, F &&fn) {
+  if (!prof_active(s)) return fn();
+  const int i = g_prof.n;
+  hipError_t e = hipEventRecord(g_prof.ev[2 * i], s);
+  if (e != hipSuccess) return e;
+  e = fn();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(g_prof.ev[2 * i + 1], s);
+  if (e != hipSuccess) return e;
+  g_prof.ids[i] = id;
+  g_prof.n = i + 1;
+  return hipSuccess;
+}
+
 size_t up256(size_t n) { return (n + 255u) / 256u * 256u; }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -46,7 +80,8 @@ bool dim_ok(int d) { return d >= 64 && d <= kMaxDim && d % kGroup == 0; }
 // workspace layout for one layer call
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t logits, sigma, h_routed, h_shared, y_shared, x_stage, hres_stage, h_pong, total;
+  size_t logits, sigma, h_routed, h_shared, y_shared, x_stage, hres_stage, xs_pairs, xs_sums,
+      h_pong, total;
 };
 
 WsLayout ws_layout(const moe_layer_t *L, int T, int n_layers) {
@@ -61,6 +96,8 @@ WsLayout ws_layout(const moe_layer_t *L, int T, int n_layers) {
   w.y_shared = o; o += up256(4 * (size_t)T * H);
   w.x_stage = o; o += up256(4 * H);
   w.hres_stage = o; o += up256(4 * H);
+  w.xs_pairs = o; o += up256(xstage_pair_bytes(L->hidden, L->bits_routed));
+  w.xs_sums = o; o += up256(xstage_sum_bytes(L->hidden, L->bits_routed));
   w.h_pong = o; o += n_layers > 0 ? up256(4 * H) : 0;
   w.total = o;
   return w;
@@ -158,6 +195,8 @@ int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in
   float *y_shared = reinterpret_cast<float *>(ws + wl.y_shared);
   float *x_stage = reinterpret_cast<float *>(ws + wl.x_stage);
   float *hres_stage = reinterpret_cast<float *>(ws + wl.hres_stage);
+  uint32_t *xs_pairs = xsrc == XS_BF16 ? reinterpret_cast<uint32_t *>(ws + wl.xs_pairs) : nullptr;
+  float *xs_sums = xsrc == XS_BF16 ? reinterpret_cast<float *>(ws + wl.xs_sums) : nullptr;
 
   // K1
   HeadParams hp = head_params(L, 1);
@@ -172,8 +211,14 @@ int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in
     hp.hres_out = hres_stage;
   }
   hp.h_shared = h_shared;
-  hp.n_shared_waves = 1;  // launcher sizes it
-  MOE_TRY_HIP(launch_head(hp, s), "router/shared launch");
+  // the shared expert's gate/up runs with the routed ones (K2) when both have
+  // the same width; otherwise here (K1)
+  const bool same_width = L->bits_shared == L->bits_routed;
+  hp.n_shared_waves = same_width ? 0 : 1;  // launcher sizes it
+  hp.bits_routed = L->bits_routed;
+  hp.xs_pairs = xs_pairs;
+  hp.xs_sums = xs_sums;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_HEAD, [&] { return launch_head(hp, s); }), "router/shared launch");
 
   // K2
   GateUpParams gp;
@@ -197,8 +242,12 @@ int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in
   gp.w_out = w;
   gp.xsrc = xsrc == XS_BF16 ? XS_BF16 : XS_F32;
   gp.x = xsrc == XS_NORM ? static_cast<const void *>(x_stage) : x;
+  gp.xs_pairs = xs_pairs;
+  gp.xs_sums = xs_sums;
   gp.h_out = h_routed;
-  MOE_TRY_HIP(launch_gateup(gp, s), "routed gate/up launch");
+  gp.with_shared = same_width;
+  gp.h_shared_out = h_shared;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_GATEUP, [&] { return launch_gateup(gp, s); }), "routed gate/up launch");
 
   // K3 (+ the shared down in its own launch when its width differs)
   DownParams dp;
@@ -212,7 +261,7 @@ int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in
   dp.off = gp.off;
   dp.soff = gp.soff;
   dp.shared_ok = 1;
-  const bool same = L->bits_shared == L->bits_routed;
+  const bool same = same_width;
   if (!same) {
     // shared expert of another width: its down projection runs on its own
     // (a null id list selects the shared record) and K3 adds sigma * y_shared
@@ -223,7 +272,7 @@ int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in
     sp.n = 1;
     sp.h = h_shared;
     sp.y = y_shared;
-    MOE_TRY_HIP(launch_down(sp, s), "shared down launch");
+    MOE_TRY_HIP(timed(s, MOE_KERNEL_DOWN_Y, [&] { return launch_down(sp, s); }), "shared down launch");
   }
   dp.combine = 1;
   dp.bits_r = L->bits_routed;
@@ -237,7 +286,7 @@ int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in
   dp.y = same ? nullptr : y_shared;
   dp.h_res = xsrc == XS_NORM ? hres_stage : h_res;
   dp.out = h_out;
-  MOE_TRY_HIP(launch_down(dp, s), "down/combine launch");
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_DOWN, [&] { return launch_down(dp, s); }), "down/combine launch");
   return MOE_OK;
 }
 
@@ -279,7 +328,7 @@ int expert_forward(const moe_layer_t *L, int bits, moe_dtype x_dtype, const void
   gp.xsrc = x_dtype == MOE_BF16 ? XS_BF16 : XS_F32;
   gp.x = x;
   gp.h_out = hbuf;
-  MOE_TRY_HIP(launch_gateup(gp, s), "gate/up launch");
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_GATEUP, [&] { return launch_gateup(gp, s); }), "gate/up launch");
 
   DownParams dp;
   memset(&dp, 0, sizeof dp);
@@ -299,7 +348,7 @@ int expert_forward(const moe_layer_t *L, int bits, moe_dtype x_dtype, const void
   dp.h = hbuf;
   dp.y = y;
   dp.shared_ok = gp.shared_ok;
-  MOE_TRY_HIP(launch_down(dp, s), "down launch");
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_DOWN_Y, [&] { return launch_down(dp, s); }), "down launch");
   return MOE_OK;
 }
 
@@ -399,7 +448,7 @@ int moe_route(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void 
   hp.logits = lg;
   hp.sigma = shared_sigma;
   hp.n_shared_waves = 0;
-  MOE_TRY_HIP(launch_head(hp, s), "router launch");
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_HEAD, [&] { return launch_head(hp, s); }), "router launch");
   TopkParams tp;
   tp.logits = lg;
   tp.T = n_tokens;
@@ -408,7 +457,7 @@ int moe_route(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void 
   tp.renorm = L->renorm_topk;
   tp.idx = topk_idx;
   tp.w = topk_w;
-  MOE_TRY_HIP(launch_topk(tp, s), "top-K launch");
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_TOPK, [&] { return launch_topk(tp, s); }), "top-K launch");
   return MOE_OK;
 }
 
@@ -446,7 +495,8 @@ int moe_combine(int hidden, int n_routed, const float *h_res, const float *y, co
   p.y_shared = y_shared;
   p.sigma = shared_sigma;
   p.out = h_out;
-  MOE_TRY_HIP(launch_combine(p, static_cast<hipStream_t>(stream)), "combine launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_COMBINE, [&] { return launch_combine(p, s); }), "combine launch");
   return MOE_OK;
 }
 
@@ -529,7 +579,8 @@ int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *up
     cur = nxt;
     nxt = t;
   }
-  if (cur != h) MOE_TRY_HIP(launch_copy_f32(h, cur, L->hidden, s), "copy launch");
+  if (cur != h)
+    MOE_TRY_HIP(timed(s, MOE_KERNEL_OTHER, [&] { return launch_copy_f32(h, cur, L->hidden, s); }), "copy launch");
   return MOE_OK;
 }
 
@@ -619,6 +670,51 @@ int moe_fill_experts(void *dst, size_t stride, int n, uint64_t seed, int layer, 
   p.off = off;
   MOE_TRY_HIP(launch_fill(p, static_cast<hipStream_t>(stream)), "fill launch");
   return MOE_OK;
+}
+
+int moe_profile_begin(int max_launches) {
+  if (max_launches < 1 || max_launches > (1 << 20)) return fail(MOE_EINVAL, "max_launches = %d", max_launches);
+  if (g_prof.on) return fail(MOE_EINVAL, "profiling already active on this thread");
+  g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+  g_prof.ids.assign(max_launches, 0);
+  for (auto &e : g_prof.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      for (auto &f : g_prof.ev)
+        if (f) (void)hipEventDestroy(f);
+      g_prof.ev.clear();
+      return hip_fail(r, "hipEventCreate");
+    }
+  }
+  g_prof.cap = max_launches;
+  g_prof.n = 0;
+  g_prof.on = true;
+  return MOE_OK;
+}
+
+int moe_profile_end(float *ms, int *kernel_ids, int capacity, int *n_out) {
+  if (!g_prof.on) return fail(MOE_EINVAL, "profiling is not active on this thread");
+  if (!n_out || (capacity > 0 && !ms)) return fail(MOE_EINVAL, "output pointer is NULL");
+  int st = MOE_OK;
+  const int n = g_prof.n < capacity ? g_prof.n : capacity;
+  if (g_prof.n > 0) {
+    hipError_t r = hipEventSynchronize(g_prof.ev[2 * (g_prof.n - 1) + 1]);
+    if (r != hipSuccess) st = hip_fail(r, "hipEventSynchronize");
+  }
+  for (int i = 0; i < n && st == MOE_OK; ++i) {
+    float t = 0.f;
+    hipError_t r = hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+    if (r != hipSuccess) st = hip_fail(r, "hipEventElapsedTime");
+    ms[i] = t;
+    if (kernel_ids) kernel_ids[i] = g_prof.ids[i];
+  }
+  *n_out = st == MOE_OK ? n : 0;
+  for (auto &e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.ids.clear();
+  g_prof.on = false;
+  g_prof.n = g_prof.cap = 0;
+  return st;
 }
 
 int moe_zero(void *ptr, size_t bytes, void *stream) {

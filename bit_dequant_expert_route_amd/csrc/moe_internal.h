@@ -55,6 +55,11 @@ struct HeadParams {
   int n_router_blocks;
   int n_shared_waves;
   int shared_rows_per_wave;
+  // bf16 x staged once for the routed experts' gate/up (written by one wave
+  // when non-null): pairs [chunks][pairs per chunk] u32, sums [chunks][2]
+  int bits_routed;
+  uint32_t *xs_pairs;
+  float *xs_sums;
 };
 hipError_t launch_head(const HeadParams &p, hipStream_t s);
 
@@ -89,7 +94,14 @@ struct GateUpParams {
   float *w_out;
   int xsrc;                       // XS_BF16 or XS_F32
   const void *x;                  // [H]
+  const uint32_t *xs_pairs;       // staged x (XS_BF16), or null -> stage here
+  const float *xs_sums;
   float *h_out;                   // [n][I]
+  // the shared expert's gate/up in the same launch (same width): its
+  // workgroups come first and need no routing
+  int with_shared;
+  float *h_shared_out;            // [I]
+  int n_shared_blocks;            // set by the launcher
   int rows_per_wave;
   int waves_per_expert;
 };
@@ -148,6 +160,10 @@ struct FillParams {
 hipError_t launch_fill(const FillParams &p, hipStream_t s);
 
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t s);
+
+// bytes of the staged-x buffers for a row of `cols` columns at `bits`
+size_t xstage_pair_bytes(int cols, int bits);
+size_t xstage_sum_bytes(int cols, int bits);
 hipError_t launch_copy_f32(float *dst, const float *src, int n, hipStream_t s);
 
 }  // namespace moe_impl

@@ -17,17 +17,20 @@
 // where the integer-weighted inner sums carry exact products: on the packed
 // bf16 dot instruction (v_dot2_f32_bf16) when x is bf16, with codes made into
 // bf16 numbers by OR-ing them into a mantissa; in fp32 FMAs after the byte
-// converts when x is fp32.  x is staged once per lane (a lane always sees the
-// same input columns) and the bias term needs only the chunk sums of x.
+// converts when x is fp32.  x is staged once (a lane always sees the same
+// input columns) and the bias term needs only the chunk sums of x.
 //
 // Memory mapping: a wave reads whole quantised rows with 128-bit loads, lane l
 // taking 16-byte chunks l, l+64, ... of a row (rows shorter than 64 chunks are
 // packed several to a wave), so every load instruction covers one contiguous
-// run of up to 1 KiB.  Rows are reduced with DPP / lane shuffles.
+// run of up to 1 KiB.  Each wave issues all of its weight loads before it
+// computes.  Rows are reduced with DPP.
 #include "moe_internal.h"
 
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 namespace moe_impl {
 
@@ -59,6 +62,10 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
 
 // Sum over aligned groups of 2^lg lanes; every lane of a group gets the sum.
 __device__ __forceinline__ float seg_sum(float v, int lg) {
@@ -72,6 +79,12 @@ __device__ __forceinline__ float seg_sum(float v, int lg) {
 }
 
 __device__ __forceinline__ float silu_mul(float a, float u) { return a / (1.0f + expf(-a)) * u; }
+
+// hide a value's provenance from the optimiser (no instruction is emitted)
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 // ---------------------------------------------------------------------------
 // staged input chunk: what one lane keeps of x for one 16-byte code chunk
@@ -155,89 +168,103 @@ __device__ __forceinline__ void stage_chunk(const float (&v)[ChunkGeom<BITS>::kC
   s.xs = xs;
 }
 
-// hide a value's provenance so that the byte-select converts are formed
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-// sum_c q_c * x_c over one 16-byte code chunk
+// sum_c q_c * x_c over one 16-byte code chunk, for two chunks at once (two
+// independent accumulation chains: gate and up, or two rows)
 template <int BITS>
-__device__ __forceinline__ float chunk_dot(const uint4 &q, const XStage<BITS, false> &s,
-                                           uint32_t kMagic16) {
-  float acc = -s.off;
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+__device__ __forceinline__ void chunk_dot2(const uint4 &qa, const uint4 &qb,
+                                           const XStage<BITS, false> &s, uint32_t magic,
+                                           float &da, float &db) {
+  float a = -s.off, b = -s.off;
+  const uint32_t wa[4] = {qa.x, qa.y, qa.z, qa.w};
+  const uint32_t wb[4] = {qb.x, qb.y, qb.z, qb.w};
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const uint32_t a = w[t] << 3, b = w[t] >> 1, c = w[t] >> 5, d = w[t] >> 9;
+    const uint32_t a3 = wa[t] << 3, a1 = wa[t] >> 1, a5 = wa[t] >> 5, a9 = wa[t] >> 9;
+    const uint32_t b3 = wb[t] << 3, b1 = wb[t] >> 1, b5 = wb[t] >> 5, b9 = wb[t] >> 9;
     if constexpr (BITS == 4) {
-      acc = dot2bf((a & 0x00780078u) | kMagic16, s.p[4 * t + 0], acc);
-      acc = dot2bf((b & 0x00780078u) | kMagic16, s.p[4 * t + 1], acc);
-      acc = dot2bf((c & 0x00780078u) | kMagic16, s.p[4 * t + 2], acc);
-      acc = dot2bf((d & 0x00780078u) | kMagic16, s.p[4 * t + 3], acc);
+      constexpr uint32_t M = 0x00780078u;
+      a = dot2bf((a3 & M) | magic, s.p[4 * t + 0], a);
+      b = dot2bf((b3 & M) | magic, s.p[4 * t + 0], b);
+      a = dot2bf((a1 & M) | magic, s.p[4 * t + 1], a);
+      b = dot2bf((b1 & M) | magic, s.p[4 * t + 1], b);
+      a = dot2bf((a5 & M) | magic, s.p[4 * t + 2], a);
+      b = dot2bf((b5 & M) | magic, s.p[4 * t + 2], b);
+      a = dot2bf((a9 & M) | magic, s.p[4 * t + 3], a);
+      b = dot2bf((b9 & M) | magic, s.p[4 * t + 3], b);
     } else {
-      acc = dot2bf((a & 0x00180018u) | kMagic16, s.p[8 * t + 0], acc);
-      acc = dot2bf((a & 0x00600060u) | kMagic16, s.p[8 * t + 1], acc);
-      acc = dot2bf((b & 0x00180018u) | kMagic16, s.p[8 * t + 2], acc);
-      acc = dot2bf((b & 0x00600060u) | kMagic16, s.p[8 * t + 3], acc);
-      acc = dot2bf((c & 0x00180018u) | kMagic16, s.p[8 * t + 4], acc);
-      acc = dot2bf((c & 0x00600060u) | kMagic16, s.p[8 * t + 5], acc);
-      acc = dot2bf((d & 0x00180018u) | kMagic16, s.p[8 * t + 6], acc);
-      acc = dot2bf((d & 0x00600060u) | kMagic16, s.p[8 * t + 7], acc);
+      constexpr uint32_t L = 0x00180018u, Hm = 0x00600060u;
+      a = dot2bf((a3 & L) | magic, s.p[8 * t + 0], a);
+      b = dot2bf((b3 & L) | magic, s.p[8 * t + 0], b);
+      a = dot2bf((a3 & Hm) | magic, s.p[8 * t + 1], a);
+      b = dot2bf((b3 & Hm) | magic, s.p[8 * t + 1], b);
+      a = dot2bf((a1 & L) | magic, s.p[8 * t + 2], a);
+      b = dot2bf((b1 & L) | magic, s.p[8 * t + 2], b);
+      a = dot2bf((a1 & Hm) | magic, s.p[8 * t + 3], a);
+      b = dot2bf((b1 & Hm) | magic, s.p[8 * t + 3], b);
+      a = dot2bf((a5 & L) | magic, s.p[8 * t + 4], a);
+      b = dot2bf((b5 & L) | magic, s.p[8 * t + 4], b);
+      a = dot2bf((a5 & Hm) | magic, s.p[8 * t + 5], a);
+      b = dot2bf((b5 & Hm) | magic, s.p[8 * t + 5], b);
+      a = dot2bf((a9 & L) | magic, s.p[8 * t + 6], a);
+      b = dot2bf((b9 & L) | magic, s.p[8 * t + 6], b);
+      a = dot2bf((a9 & Hm) | magic, s.p[8 * t + 7], a);
+      b = dot2bf((b9 & Hm) | magic, s.p[8 * t + 7], b);
     }
   }
-  return acc;
+  da = a;
+  db = b;
 }
 
 template <int BITS>
-__device__ __forceinline__ float chunk_dot(const uint4 &q, const XStage<BITS, true> &s) {
-  float acc = 0.f;
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+__device__ __forceinline__ void chunk_dot2(const uint4 &qa, const uint4 &qb,
+                                           const XStage<BITS, true> &s, uint32_t,
+                                           float &da, float &db) {
+  float a = 0.f, b = 0.f;
+  const uint32_t wa[4] = {qa.x, qa.y, qa.z, qa.w};
+  const uint32_t wb[4] = {qb.x, qb.y, qb.z, qb.w};
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     if constexpr (BITS == 4) {
       // bytes of lo: nibbles 0,2,4,6; bytes of hi: nibbles 1,3,5,7
-      const uint32_t lo = opaque(w[t] & 0x0F0F0F0Fu);
-      const uint32_t hi = opaque((w[t] >> 4) & 0x0F0F0F0Fu);
+      const uint32_t la = opaque(wa[t] & 0x0F0F0F0Fu), ha = opaque((wa[t] >> 4) & 0x0F0F0F0Fu);
+      const uint32_t lb = opaque(wb[t] & 0x0F0F0F0Fu), hb = opaque((wb[t] >> 4) & 0x0F0F0F0Fu);
       const float *x = s.v + 8 * t;
-      acc = fmaf((float)(lo & 0xFFu), x[0], acc);
-      acc = fmaf((float)(hi & 0xFFu), x[1], acc);
-      acc = fmaf((float)((lo >> 8) & 0xFFu), x[2], acc);
-      acc = fmaf((float)((hi >> 8) & 0xFFu), x[3], acc);
-      acc = fmaf((float)((lo >> 16) & 0xFFu), x[4], acc);
-      acc = fmaf((float)((hi >> 16) & 0xFFu), x[5], acc);
-      acc = fmaf((float)(lo >> 24), x[6], acc);
-      acc = fmaf((float)(hi >> 24), x[7], acc);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t sh = 8 * k;
+        const float xl = x[2 * k], xh = x[2 * k + 1];
+        const uint32_t qla = k == 3 ? (la >> 24) : ((la >> sh) & 0xFFu);
+        const uint32_t qlb = k == 3 ? (lb >> 24) : ((lb >> sh) & 0xFFu);
+        const uint32_t qha = k == 3 ? (ha >> 24) : ((ha >> sh) & 0xFFu);
+        const uint32_t qhb = k == 3 ? (hb >> 24) : ((hb >> sh) & 0xFFu);
+        a = fmaf((float)qla, xl, a);
+        b = fmaf((float)qlb, xl, b);
+        a = fmaf((float)qha, xh, a);
+        b = fmaf((float)qhb, xh, b);
+      }
     } else {
-      // byte b of f_k is field 4b + k
-      const uint32_t f0 = opaque(w[t] & 0x03030303u);
-      const uint32_t f1 = opaque((w[t] >> 2) & 0x03030303u);
-      const uint32_t f2 = opaque((w[t] >> 4) & 0x03030303u);
-      const uint32_t f3 = opaque((w[t] >> 6) & 0x03030303u);
+      // byte bb of f_k is field 4*bb + k
+      uint32_t fa[4], fb[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        fa[k] = opaque((wa[t] >> (2 * k)) & 0x03030303u);
+        fb[k] = opaque((wb[t] >> (2 * k)) & 0x03030303u);
+      }
       const float *x = s.v + 16 * t;
-      const uint32_t f[4] = {f0, f1, f2, f3};
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t byte = bb == 3 ? (f[k] >> 24) : ((f[k] >> (8 * bb)) & 0xFFu);
-          acc = fmaf((float)byte, x[4 * bb + k], acc);
+          const uint32_t qa8 = bb == 3 ? (fa[k] >> 24) : ((fa[k] >> (8 * bb)) & 0xFFu);
+          const uint32_t qb8 = bb == 3 ? (fb[k] >> 24) : ((fb[k] >> (8 * bb)) & 0xFFu);
+          a = fmaf((float)qa8, x[4 * bb + k], a);
+          b = fmaf((float)qb8, x[4 * bb + k], b);
         }
       }
     }
   }
-  return acc;
-}
-
-template <int BITS>
-__device__ __forceinline__ float chunk_dot_any(const uint4 &q, const XStage<BITS, false> &s,
-                                               uint32_t magic) {
-  return chunk_dot<BITS>(q, s, magic);
-}
-template <int BITS>
-__device__ __forceinline__ float chunk_dot_any(const uint4 &q, const XStage<BITS, true> &s,
-                                               uint32_t) {
-  return chunk_dot<BITS>(q, s);
+  da = a;
+  db = b;
 }
 
 // load the x values of one chunk (columns col0 .. col0 + kCols - 1) as fp32
@@ -255,21 +282,84 @@ __device__ __forceinline__ void load_x_chunk(const void *x, const float *xl, int
       v[8 * i + 4] = bf_lo(u.z); v[8 * i + 5] = bf_hi(u.z);
       v[8 * i + 6] = bf_lo(u.w); v[8 * i + 7] = bf_hi(u.w);
     }
-  } else if constexpr (XS == XS_F32) {
-    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + col0);
-#pragma unroll
-    for (int i = 0; i < NC / 4; ++i) {
-      const float4 u = p[i];
-      v[4 * i + 0] = u.x; v[4 * i + 1] = u.y; v[4 * i + 2] = u.z; v[4 * i + 3] = u.w;
-    }
   } else {
-    const float4 *p = reinterpret_cast<const float4 *>(xl + col0);
+    const float *src = (XS == XS_F32) ? static_cast<const float *>(x) : xl;
+    const float4 *p = reinterpret_cast<const float4 *>(src + col0);
 #pragma unroll
     for (int i = 0; i < NC / 4; ++i) {
       const float4 u = p[i];
       v[4 * i + 0] = u.x; v[4 * i + 1] = u.y; v[4 * i + 2] = u.z; v[4 * i + 3] = u.w;
     }
   }
+}
+
+// raw x of one chunk as loaded (bf16 words or fp32), before the staging math;
+// loading and staging are separate so that other loads can be issued between
+template <int BITS, int XS>
+struct XRaw {
+  static constexpr int kN = (XS == XS_BF16) ? ChunkGeom<BITS>::kCols / 8 : ChunkGeom<BITS>::kCols / 4;
+  uint4 u[kN];
+};
+
+template <int BITS, int XS>
+__device__ __forceinline__ XRaw<BITS, XS> load_raw(const void *x, const float *xl, int c) {
+  XRaw<BITS, XS> r;
+  const int col0 = c * ChunkGeom<BITS>::kCols;
+  const uint4 *p;
+  if constexpr (XS == XS_BF16) p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + col0);
+  else p = reinterpret_cast<const uint4 *>(((XS == XS_F32) ? static_cast<const float *>(x) : xl) + col0);
+#pragma unroll
+  for (int i = 0; i < XRaw<BITS, XS>::kN; ++i) r.u[i] = p[i];
+  return r;
+}
+
+template <int BITS, int XS>
+__device__ __forceinline__ XStage<BITS, XS != XS_BF16> stage_raw(const XRaw<BITS, XS> &r) {
+  float v[ChunkGeom<BITS>::kCols];
+#pragma unroll
+  for (int i = 0; i < XRaw<BITS, XS>::kN; ++i) {
+    const uint4 u = r.u[i];
+    if constexpr (XS == XS_BF16) {
+      v[8 * i + 0] = bf_lo(u.x); v[8 * i + 1] = bf_hi(u.x);
+      v[8 * i + 2] = bf_lo(u.y); v[8 * i + 3] = bf_hi(u.y);
+      v[8 * i + 4] = bf_lo(u.z); v[8 * i + 5] = bf_hi(u.z);
+      v[8 * i + 6] = bf_lo(u.w); v[8 * i + 7] = bf_hi(u.w);
+    } else {
+      v[4 * i + 0] = __uint_as_float(u.x); v[4 * i + 1] = __uint_as_float(u.y);
+      v[4 * i + 2] = __uint_as_float(u.z); v[4 * i + 3] = __uint_as_float(u.w);
+    }
+  }
+  XStage<BITS, XS != XS_BF16> s;
+  stage_chunk<BITS>(v, s);
+  return s;
+}
+
+// stage chunk c of x from x itself
+template <int BITS, int XS>
+__device__ __forceinline__ XStage<BITS, XS != XS_BF16> make_stage(const void *x, const float *xl,
+                                                                  int c) {
+  return stage_raw<BITS, XS>(load_raw<BITS, XS>(x, xl, c));
+}
+
+// chunk c of bf16 x as staged once into global memory (write_xstage)
+template <int BITS>
+__device__ __forceinline__ XStage<BITS, false> read_stage(const uint32_t *xs_pairs,
+                                                          const float *xs_sums, int c) {
+  constexpr int NP = ChunkGeom<BITS>::kPairs;
+  XStage<BITS, false> s;
+  const uint4 *pp = reinterpret_cast<const uint4 *>(xs_pairs + (size_t)c * NP);
+#pragma unroll
+  for (int i = 0; i < NP / 4; ++i) {
+    const uint4 u = pp[i];
+    s.p[4 * i + 0] = u.x;
+    s.p[4 * i + 1] = u.y;
+    s.p[4 * i + 2] = u.z;
+    s.p[4 * i + 3] = u.w;
+  }
+  const float2 sm = reinterpret_cast<const float2 *>(xs_sums)[c];
+  s.off = sm.x;
+  s.xs = sm.y;
+  return s;
 }
 
 // lane layout over rows of `cols` columns at BITS bits
@@ -302,55 +392,52 @@ template <int BITS>
 __device__ __forceinline__ int chunk_group(int c) { return BITS == 4 ? (c >> 1) : c; }
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU for rows [row0, row0 + NPASS*rpp) of one expert
-// ([openclawradar] "Metal compute shaders": fused SwiGLU; h = silu(a) * u)
+// gate/up + SwiGLU ([openclawradar] "Metal compute shaders": fused SwiGLU;
+// h = silu(a) * u with a = W_gate x, u = W_up x)
 // ---------------------------------------------------------------------------
-template <int BITS, int NCH, int NPASS, int XS>
-__device__ __forceinline__ void gateup_wave(const uint8_t *rec, const RecOffsets &off,
-                                            int H, int I, int row0, bool valid,
-                                            const void *x, const float *xl, float *h_out) {
-  constexpr bool XF32 = (XS != XS_BF16);
-  const RowMap m = row_map<BITS>(H);
+template <int BITS, int NCH, int NPASS>
+struct GUTile {
+  uint4 gq[NPASS][NCH], uq[NPASS][NCH];
+  uint32_t gs[NPASS][NCH], us[NPASS][NCH];
+};
+
+// Every lane loads (row 0 / chunk 0 stand in for positions past the end, so
+// each address is valid); what lies outside is masked where it is used.  With
+// no branch or use next to them, the loads are all in flight before the first
+// wait.
+template <int BITS, int NCH, int NPASS>
+__device__ __forceinline__ void gu_load(GUTile<BITS, NCH, NPASS> &t, const uint8_t *rec,
+                                        const RecOffsets &off, const RowMap &m, int I, int row0) {
   const uint32_t *gc = reinterpret_cast<const uint32_t *>(rec + off.gate_codes);
   const uint32_t *uc = reinterpret_cast<const uint32_t *>(rec + off.up_codes);
   const uint32_t *gs = reinterpret_cast<const uint32_t *>(rec + off.gate_sb);
   const uint32_t *us = reinterpret_cast<const uint32_t *>(rec + off.up_sb);
-
-  uint4 gq[NPASS][NCH], uq[NPASS][NCH];
-  uint32_t gsw[NPASS][NCH], usw[NPASS][NCH];
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) {
     const int r = row0 + p * m.rpp + m.rip;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = m.li + (j << m.lg);
-      if (valid && r < I && c < m.cpr) {
-        const size_t wo = (size_t)r * m.wpr + (size_t)c * 4;
-        gq[p][j] = *reinterpret_cast<const uint4 *>(gc + wo);
-        uq[p][j] = *reinterpret_cast<const uint4 *>(uc + wo);
-        const size_t so = (size_t)r * m.gpr + chunk_group<BITS>(c);
-        gsw[p][j] = gs[so];
-        usw[p][j] = us[so];
-      } else {
-        gq[p][j] = make_uint4(0, 0, 0, 0);
-        uq[p][j] = make_uint4(0, 0, 0, 0);
-        gsw[p][j] = 0;
-        usw[p][j] = 0;
-      }
+      const bool in = r < I && c < m.cpr;
+      const int rr = in ? r : 0, cc = in ? c : 0;
+      const size_t wo = (size_t)rr * m.wpr + (size_t)cc * 4;
+      const size_t so = (size_t)rr * m.gpr + chunk_group<BITS>(cc);
+      t.gq[p][j] = *reinterpret_cast<const uint4 *>(gc + wo);
+      t.uq[p][j] = *reinterpret_cast<const uint4 *>(uc + wo);
+      t.gs[p][j] = gs[so];
+      t.us[p][j] = us[so];
     }
   }
+}
 
-  XStage<BITS, XF32> xs[NCH];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = m.li + (j << m.lg);
-    if (c < m.cpr) {
-      float v[ChunkGeom<BITS>::kCols];
-      load_x_chunk<BITS, XS>(x, xl, c * ChunkGeom<BITS>::kCols, v);
-      stage_chunk<BITS>(v, xs[j]);
-    }
-  }
+__device__ __forceinline__ bool in_tile(const RowMap &m, int rows, int row0, int p, int j) {
+  return row0 + p * m.rpp + m.rip < rows && m.li + (j << m.lg) < m.cpr;
+}
 
+template <int BITS, int NCH, int NPASS, bool XF32>
+__device__ __forceinline__ void gu_compute(const GUTile<BITS, NCH, NPASS> &t,
+                                           const XStage<BITS, XF32> (&xs)[NCH], const RowMap &m,
+                                           int I, int row0, bool valid, float *h_out) {
   // the magic constant lives in a VGPR so that mask-and-or is one v_and_or_b32
   // (gfx9 VOP3 reads at most one scalar or literal operand)
   const uint32_t magic = opaque(kMagic16);
@@ -359,13 +446,13 @@ __device__ __forceinline__ void gateup_wave(const uint8_t *rec, const RecOffsets
     float a = 0.f, u = 0.f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int c = m.li + (j << m.lg);
-      if (c < m.cpr) {
-        const float da = chunk_dot_any<BITS>(gq[p][j], xs[j], magic);
-        const float du = chunk_dot_any<BITS>(uq[p][j], xs[j], magic);
-        a = fmaf(bf_lo(gsw[p][j]), da, fmaf(bf_hi(gsw[p][j]), xs[j].xs, a));
-        u = fmaf(bf_lo(usw[p][j]), du, fmaf(bf_hi(usw[p][j]), xs[j].xs, u));
-      }
+      // positions past the end get zero scale and bias
+      const bool in = in_tile(m, I, row0, p, j);
+      const uint32_t gsw = in ? t.gs[p][j] : 0u, usw = in ? t.us[p][j] : 0u;
+      float da, du;
+      chunk_dot2<BITS>(t.gq[p][j], t.uq[p][j], xs[j], magic, da, du);
+      a = fmaf(bf_lo(gsw), da, fmaf(bf_hi(gsw), xs[j].xs, a));
+      u = fmaf(bf_lo(usw), du, fmaf(bf_hi(usw), xs[j].xs, u));
     }
     a = seg_sum(a, m.lg);
     u = seg_sum(u, m.lg);
@@ -375,174 +462,197 @@ __device__ __forceinline__ void gateup_wave(const uint8_t *rec, const RecOffsets
 }
 
 // ---------------------------------------------------------------------------
-// top-K of E logits by one wave: K selection rounds of a wave arg-max, ties to
-// the lower index; then softmax weights of the selected experts
+// top-K of E logits by one workgroup: K selection rounds of an arg-max (ties
+// to the lower index), then the softmax weights of the selected experts
 // ([openclawradar] "Pipeline performance": softmax + topK routing)
 // ---------------------------------------------------------------------------
-struct TopK {
+struct TopKShared {
   int idx[kMaxK];
   float w[kMaxK];
+  float rv[kBlock / 64];
+  int re[kBlock / 64];
+  float z[kBlock / 64];
 };
 
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+__device__ __forceinline__ void argmax_merge(float &v, int &e, float ov, int oe) {
+  if (ov > v || (ov == v && oe < e)) {
+    v = ov;
+    e = oe;
+  }
 }
 
-__device__ TopK wave_topk(const float *__restrict__ lg, int E, int K, int renorm) {
-  const int lane = lane_id();
-  constexpr int NV = kMaxE / 64;
+// arg-max over the wave; the result is returned in every lane
+__device__ __forceinline__ void wave_argmax(float &v, int &e) {
+  argmax_merge(v, e, dpp<0xB1>(v), dpp_i<0xB1>(e));
+  argmax_merge(v, e, dpp<0x4E>(v), dpp_i<0x4E>(e));
+  argmax_merge(v, e, dpp<0x141>(v), dpp_i<0x141>(e));
+  argmax_merge(v, e, dpp<0x140>(v), dpp_i<0x140>(e));
+  // every lane of each 16-lane row now holds its row's best
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int be = __builtin_amdgcn_readlane(e, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    argmax_merge(bv, be, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r)),
+                 __builtin_amdgcn_readlane(e, 16 * r));
+  v = bv;
+  e = be;
+}
+
+// every thread of the (256-thread) workgroup must call this
+__device__ void block_topk(const float *__restrict__ lg, int E, int K, int renorm,
+                           TopKShared &sh) {
+  constexpr int NV = kMaxE / kBlock;
+  constexpr int kNone = 0x7fffffff;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   float v[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int e = lane + 64 * i;
+    const int e = tid + kBlock * i;
     v[i] = e < E ? lg[e] : -INFINITY;
   }
   uint32_t taken = 0;
-  TopK r;
   float lk[kMaxK];
+  int ik[kMaxK];
 #pragma unroll
   for (int k = 0; k < kMaxK; ++k) {
-    r.idx[k] = -2;
-    r.w[k] = 0.f;
     lk[k] = -INFINITY;
+    ik[k] = kNone;
     if (k < K) {
       float bv = -INFINITY;
-      int bi = 0x7fffffff;
+      int be = kNone;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
-          bv = v[i];
-          bi = e;
-        }
+        const int e = tid + kBlock * i;
+        if (e < E && !((taken >> i) & 1u)) argmax_merge(bv, be, v[i], e);
       }
+      wave_argmax(bv, be);
+      if (lane == 0) {
+        sh.rv[wv] = bv;
+        sh.re[wv] = be;
+      }
+      __syncthreads();
+      bv = sh.rv[0];
+      be = sh.re[0];
 #pragma unroll
-      for (int msk = 32; msk >= 1; msk >>= 1) {
-        const float ov = __shfl_xor(bv, msk, 64);
-        const int oi = __shfl_xor(bi, msk, 64);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (bi != 0x7fffffff && (bi & 63) == lane) taken |= 1u << (bi >> 6);
-      r.idx[k] = bi == 0x7fffffff ? -2 : bi;
+      for (int w = 1; w < kBlock / 64; ++w) argmax_merge(bv, be, sh.rv[w], sh.re[w]);
+      __syncthreads();
+      if (be != kNone && (be % kBlock) == tid) taken |= 1u << (be / kBlock);
       lk[k] = bv;
+      ik[k] = be;
     }
   }
   const float mx = lk[0];
-  float z = 0.f;
+  float den;
+  if (renorm) {
+    den = 0.f;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + 64 * i;
-    if (e < E) z += expf(v[i] - mx);
+    for (int k = 0; k < kMaxK; ++k)
+      if (k < K) den += expf(lk[k] - mx);
+  } else {
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (tid + kBlock * i < E) z += expf(v[i] - mx);
+    z = seg_sum(z, 6);
+    if (lane == 0) sh.z[wv] = z;
+    __syncthreads();
+    den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) den += sh.z[w];
   }
-  z = seg_sum(z, 6);
-  float zk = 0.f;
+  if (tid < K) {
+    int e = kNone;
+    float l = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < kMaxK; ++k)
-    if (k < K) zk += expf(lk[k] - mx);
-  const float den = renorm ? zk : z;
-#pragma unroll
-  for (int k = 0; k < kMaxK; ++k) {
-    if (k < K) r.w[k] = r.idx[k] < 0 ? __builtin_nanf("") : expf(lk[k] - mx) / den;
+    for (int k = 0; k < kMaxK; ++k)
+      if (k == tid) {
+        e = ik[k];
+        l = lk[k];
+      }
+    sh.idx[tid] = e == kNone ? -2 : e;
+    sh.w[tid] = e == kNone ? __builtin_nanf("") : expf(l - mx) / den;
   }
-  return r;
-}
-
-__device__ __forceinline__ int pick_idx(const TopK &t, int k) {
-  int v = -2;
-#pragma unroll
-  for (int i = 0; i < kMaxK; ++i)
-    if (i == k) v = t.idx[i];
-  return v;
-}
-
-__device__ __forceinline__ void write_topk(const TopK &t, int K, int32_t *idx, float *w) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int i = 0; i < kMaxK; ++i) {
-    if (i < K && lane == i) {
-      if (idx) idx[i] = t.idx[i];
-      if (w) w[i] = t.w[i];
-    }
-  }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// K1: router rows, shared-gate row, shared expert gate/up
+// K1: router rows, shared-gate row, shared expert gate/up, x staging
 // ---------------------------------------------------------------------------
 // dot of a router/gate row with x for token t; every lane reads 16-byte
-// chunks lane, lane+64, ... of the row.  fp32 accumulation per lane, then a
-// 6-step tree: reduction depth stays <= 70 for H = 4096, which bounds the
-// fp32 error of a logit well below the top-K gap.
+// chunks lane, lane+64, ... of the row.  fp32 accumulation in two chains per
+// lane, then a 6-step tree: reduction depth stays <= 40 for H = 4096, which
+// bounds the fp32 error of a logit well below the top-K gap.
 template <int XS>
 __device__ __forceinline__ float row_dot(const void *row, int dtype, int H, const void *x,
                                          const float *xl, int t) {
   const int lane = lane_id();
-  float acc = 0.f;
-  if (dtype == 1) {  // bf16 row
+  float acc0 = 0.f, acc1 = 0.f;
+  if (dtype == 1) {  // bf16 row: chunk c = columns 8c .. 8c+7
     const uint4 *W = static_cast<const uint4 *>(row);
     const int U = H / 8;
     for (int j0 = 0; j0 < U; j0 += 64 * 8) {
       uint4 wv[8];
+      float4 xa[8], xb[8];
+      uint4 xh[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int c = j0 + jj * 64 + lane;
-        wv[jj] = c < U ? W[c] : make_uint4(0, 0, 0, 0);
+        const int cc = c < U ? c : 0;
+        wv[jj] = W[cc];
+        if constexpr (XS == XS_BF16) {
+          xh[jj] = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (size_t)t * H)[cc];
+        } else {
+          const float *xf = (XS == XS_F32) ? static_cast<const float *>(x) + (size_t)t * H : xl;
+          xa[jj] = reinterpret_cast<const float4 *>(xf)[2 * cc];
+          xb[jj] = reinterpret_cast<const float4 *>(xf)[2 * cc + 1];
+        }
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        const int c = j0 + jj * 64 + lane;
-        if (c < U) {
-          const uint32_t w4[4] = {wv[jj].x, wv[jj].y, wv[jj].z, wv[jj].w};
-          if constexpr (XS == XS_BF16) {
-            const uint4 xv = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (size_t)t * H)[c];
-            acc = dot2bf(w4[0], xv.x, acc);
-            acc = dot2bf(w4[1], xv.y, acc);
-            acc = dot2bf(w4[2], xv.z, acc);
-            acc = dot2bf(w4[3], xv.w, acc);
-          } else {
-            const float *xf = (XS == XS_F32) ? static_cast<const float *>(x) + (size_t)t * H : xl;
-            const float4 a = reinterpret_cast<const float4 *>(xf)[2 * c];
-            const float4 b = reinterpret_cast<const float4 *>(xf)[2 * c + 1];
-            acc = fmaf(bf_lo(w4[0]), a.x, acc); acc = fmaf(bf_hi(w4[0]), a.y, acc);
-            acc = fmaf(bf_lo(w4[1]), a.z, acc); acc = fmaf(bf_hi(w4[1]), a.w, acc);
-            acc = fmaf(bf_lo(w4[2]), b.x, acc); acc = fmaf(bf_hi(w4[2]), b.y, acc);
-            acc = fmaf(bf_lo(w4[3]), b.z, acc); acc = fmaf(bf_hi(w4[3]), b.w, acc);
-          }
+        const bool in = j0 + jj * 64 + lane < U;
+        const uint4 w = in ? wv[jj] : make_uint4(0, 0, 0, 0);
+        if constexpr (XS == XS_BF16) {
+          acc0 = dot2bf(w.x, xh[jj].x, acc0);
+          acc1 = dot2bf(w.y, xh[jj].y, acc1);
+          acc0 = dot2bf(w.z, xh[jj].z, acc0);
+          acc1 = dot2bf(w.w, xh[jj].w, acc1);
+        } else {
+          const float4 a = xa[jj], b = xb[jj];
+          acc0 = fmaf(bf_lo(w.x), a.x, acc0); acc1 = fmaf(bf_hi(w.x), a.y, acc1);
+          acc0 = fmaf(bf_lo(w.y), a.z, acc0); acc1 = fmaf(bf_hi(w.y), a.w, acc1);
+          acc0 = fmaf(bf_lo(w.z), b.x, acc0); acc1 = fmaf(bf_hi(w.z), b.y, acc1);
+          acc0 = fmaf(bf_lo(w.w), b.z, acc0); acc1 = fmaf(bf_hi(w.w), b.w, acc1);
         }
       }
     }
-  } else {  // fp32 row
+  } else {  // fp32 row: chunk c = columns 4c .. 4c+3
     const float4 *W = static_cast<const float4 *>(row);
     const int U = H / 4;
     for (int j0 = 0; j0 < U; j0 += 64 * 8) {
-      float4 wv[8];
+      float4 wv[8], xv[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int c = j0 + jj * 64 + lane;
-        wv[jj] = c < U ? W[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int cc = c < U ? c : 0;
+        wv[jj] = W[cc];
+        if constexpr (XS == XS_BF16) {
+          const uint2 u = reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + (size_t)t * H)[cc];
+          xv[jj] = make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y));
+        } else {
+          const float *xf = (XS == XS_F32) ? static_cast<const float *>(x) + (size_t)t * H : xl;
+          xv[jj] = reinterpret_cast<const float4 *>(xf)[cc];
+        }
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        const int c = j0 + jj * 64 + lane;
-        if (c < U) {
-          float4 xv;
-          if constexpr (XS == XS_BF16) {
-            const uint2 u = reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + (size_t)t * H)[c];
-            xv = make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y));
-          } else {
-            const float *xf = (XS == XS_F32) ? static_cast<const float *>(x) + (size_t)t * H : xl;
-            xv = reinterpret_cast<const float4 *>(xf)[c];
-          }
-          acc = fmaf(wv[jj].x, xv.x, acc); acc = fmaf(wv[jj].y, xv.y, acc);
-          acc = fmaf(wv[jj].z, xv.z, acc); acc = fmaf(wv[jj].w, xv.w, acc);
-        }
+        const bool in = j0 + jj * 64 + lane < U;
+        const float4 w = in ? wv[jj] : make_float4(0.f, 0.f, 0.f, 0.f);
+        acc0 = fmaf(w.x, xv[jj].x, acc0); acc1 = fmaf(w.y, xv[jj].y, acc1);
+        acc0 = fmaf(w.z, xv[jj].z, acc0); acc1 = fmaf(w.w, xv[jj].w, acc1);
       }
     }
   }
-  return seg_sum(acc, 6);
+  return seg_sum(acc0 + acc1, 6);
 }
 
 // x = (h + u) / sqrt(mean((h + u)^2) + 1e-6) into LDS, two passes
@@ -577,6 +687,24 @@ __device__ __forceinline__ void norm_prologue(const HeadParams &p, float *xl) {
   __syncthreads();
 }
 
+// one wave stages bf16 x for every chunk of a row at BITS and stores it
+template <int BITS>
+__device__ __forceinline__ void write_xstage(const void *x, int H, uint32_t *pairs, float *sums) {
+  constexpr int NP = ChunkGeom<BITS>::kPairs;
+  const int cpr = H / ChunkGeom<BITS>::kCols;
+  for (int c = lane_id(); c < cpr; c += 64) {
+    XStage<BITS, false> s;
+    float v[ChunkGeom<BITS>::kCols];
+    load_x_chunk<BITS, XS_BF16>(x, nullptr, c * ChunkGeom<BITS>::kCols, v);
+    stage_chunk<BITS>(v, s);
+    uint4 *pp = reinterpret_cast<uint4 *>(pairs + (size_t)c * NP);
+#pragma unroll
+    for (int i = 0; i < NP / 4; ++i)
+      pp[i] = make_uint4(s.p[4 * i], s.p[4 * i + 1], s.p[4 * i + 2], s.p[4 * i + 3]);
+    reinterpret_cast<float2 *>(sums)[c] = make_float2(s.off, s.xs);
+  }
+}
+
 template <int XS, int BITS_S, int NCH_S, int NPASS_S>
 __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
   extern __shared__ float xl[];
@@ -584,8 +712,17 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
   const int wv = wave_uniform(threadIdx.x >> 6);
   const int blk = wave_uniform(blockIdx.x);
   if (blk < p.n_router_blocks) {
-    const int unit = blk * (kBlock / 64) + wv;  // (token, row) pairs
+    const int unit = blk * (kBlock / 64) + wv;  // (token, row) pairs, then the x stager
     const int rows = p.E + 1;
+    if (unit == p.T * rows) {
+      if constexpr (XS == XS_BF16) {
+        if (p.xs_pairs) {
+          if (p.bits_routed == 4) write_xstage<4>(p.x, p.H, p.xs_pairs, p.xs_sums);
+          else write_xstage<2>(p.x, p.H, p.xs_pairs, p.xs_sums);
+        }
+      }
+      return;
+    }
     const int t = unit / rows, row = unit - t * rows;
     if (t >= p.T) return;
     if (row < p.E) {
@@ -602,54 +739,123 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
   if constexpr (BITS_S != 0) {
     const int sw = (blk - p.n_router_blocks) * (kBlock / 64) + wv;
     if (sw >= p.n_shared_waves) return;
-    gateup_wave<BITS_S, NCH_S, NPASS_S, XS>(p.shared_rec, p.soff, p.H, p.I,
-                                            sw * p.shared_rows_per_wave, true, p.x, xl,
-                                            p.h_shared);
+    constexpr bool XF32 = XS != XS_BF16;
+    const RowMap m = row_map<BITS_S>(p.H);
+    const int row0 = sw * p.shared_rows_per_wave;
+    XRaw<BITS_S, XS> xr[NCH_S];
+#pragma unroll
+    for (int j = 0; j < NCH_S; ++j) {
+      const int c = m.li + (j << m.lg);
+      xr[j] = load_raw<BITS_S, XS>(p.x, xl, c < m.cpr ? c : 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    GUTile<BITS_S, NCH_S, NPASS_S> tile;
+    gu_load(tile, p.shared_rec, p.soff, m, p.I, row0);
+    __builtin_amdgcn_sched_barrier(0);
+    XStage<BITS_S, XF32> xs[NCH_S];
+#pragma unroll
+    for (int j = 0; j < NCH_S; ++j) xs[j] = stage_raw<BITS_S, XS>(xr[j]);
+    gu_compute(tile, xs, m, p.I, row0, true, p.h_shared);
   }
 }
 
 // ---------------------------------------------------------------------------
-// stand-alone top-K (one wave per token)
+// stand-alone top-K (one workgroup per token)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_topk(TopkParams p) {
+__global__ __launch_bounds__(kBlock) void k_topk(TopkParams p) {
+  __shared__ TopKShared sh;
   const int t = blockIdx.x;
-  const TopK r = wave_topk(p.logits + (size_t)t * p.E, p.E, p.K, p.renorm);
-  write_topk(r, p.K, p.idx + (size_t)t * p.K, p.w + (size_t)t * p.K);
+  block_topk(p.logits + (size_t)t * p.E, p.E, p.K, p.renorm, sh);
+  if ((int)threadIdx.x < p.K) {
+    p.idx[(size_t)t * p.K + threadIdx.x] = sh.idx[threadIdx.x];
+    p.w[(size_t)t * p.K + threadIdx.x] = sh.w[threadIdx.x];
+  }
 }
 
 // ---------------------------------------------------------------------------
-// K2: gate/up for a list of experts
+// K2: gate/up for a list of experts (explicit ids, or the top-K of the
+// logits, computed by every workgroup)
 // ---------------------------------------------------------------------------
 template <int BITS, int NCH, int NPASS, int XS>
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
-  const int wave = wave_uniform(blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6));
-  const int slot = wave / p.waves_per_expert;
-  if (slot >= p.n) return;
-  const int wie = wave - slot * p.waves_per_expert;
-  int id;
-  if (p.ids) {
-    id = wave_uniform(p.ids[slot]);
+  __shared__ TopKShared sh;
+  const int blk = wave_uniform(blockIdx.x);
+  const int wv = wave_uniform(threadIdx.x >> 6);
+  int id, wie;
+  float *hout;
+  if (blk < p.n_shared_blocks) {
+    // the shared expert does not depend on the routing: these workgroups
+    // stream its rows while the routed ones are still selecting experts
+    wie = blk * (kBlock / 64) + wv;
+    if (wie >= p.waves_per_expert) return;
+    id = kSharedId;
+    hout = p.h_shared_out;
   } else {
-    const TopK t = wave_topk(p.logits, p.E, p.K, p.renorm);
-    id = wave_uniform(pick_idx(t, slot));
-    if (wave == 0) write_topk(t, p.K, p.idx_out, p.w_out);
+    const int wave = (blk - p.n_shared_blocks) * (kBlock / 64) + wv;
+    if (!p.ids) {
+      block_topk(p.logits, p.E, p.K, p.renorm, sh);
+      if (blk == p.n_shared_blocks && (int)threadIdx.x < p.K) {
+        if (p.idx_out) p.idx_out[threadIdx.x] = sh.idx[threadIdx.x];
+        if (p.w_out) p.w_out[threadIdx.x] = sh.w[threadIdx.x];
+      }
+    }
+    const int slot = wave / p.waves_per_expert;
+    if (slot >= p.n) return;
+    wie = wave - slot * p.waves_per_expert;
+    id = wave_uniform(p.ids ? p.ids[slot] : sh.idx[slot]);
+    hout = p.h_out + (size_t)slot * p.I;
   }
   const bool shared = id == kSharedId;
   const bool valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
   const uint8_t *rec = shared ? p.shared_rec : p.experts + (size_t)(valid ? id : 0) * p.stride;
-  gateup_wave<BITS, NCH, NPASS, XS>(rec, shared ? p.soff : p.off, p.H, p.I,
-                                    wie * p.rows_per_wave, valid, p.x, nullptr,
-                                    p.h_out + (size_t)slot * p.I);
+  constexpr bool XF32 = XS != XS_BF16;
+  const RowMap m = row_map<BITS>(p.H);
+  const int row0 = wie * p.rows_per_wave;
+  // x loads first, then the weight loads, then the staging math: vmcnt is in
+  // order, so the staging waits only for x
+  XStage<BITS, XF32> xs[NCH];
+  XRaw<BITS, XS> xr[NCH];
+  bool from_buf = false;
+  if constexpr (XS == XS_BF16) from_buf = p.xs_pairs != nullptr;
+  if (from_buf) {
+    if constexpr (XS == XS_BF16) {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int c = m.li + (j << m.lg);
+        xs[j] = read_stage<BITS>(p.xs_pairs, p.xs_sums, c < m.cpr ? c : 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = m.li + (j << m.lg);
+      xr[j] = load_raw<BITS, XS>(p.x, nullptr, c < m.cpr ? c : 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  GUTile<BITS, NCH, NPASS> tile;
+  gu_load(tile, rec, shared ? p.soff : p.off, m, p.I, row0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (!from_buf) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) xs[j] = stage_raw<BITS, XS>(xr[j]);
+  }
+  gu_compute(tile, xs, m, p.I, row0, valid, hout);
 }
 
 // ---------------------------------------------------------------------------
 // K3: down projection
 // ---------------------------------------------------------------------------
-// one expert, rows [row0, row0 + NPASS*rpp): issue the loads
 template <int BITS, int NCH, int NPASS>
-__device__ __forceinline__ void down_load(const uint8_t *rec, const RecOffsets &off, int H,
-                                          const RowMap &m, int row0, bool valid,
-                                          uint4 (&q)[NPASS][NCH], uint32_t (&sb)[NPASS][NCH]) {
+struct DnTile {
+  uint4 q[NPASS][NCH];
+  uint32_t sb[NPASS][NCH];
+};
+
+template <int BITS, int NCH, int NPASS>
+__device__ __forceinline__ void down_load(DnTile<BITS, NCH, NPASS> &t, const uint8_t *rec,
+                                          const RecOffsets &off, int H, const RowMap &m,
+                                          int row0) {
   const uint32_t *dc = reinterpret_cast<const uint32_t *>(rec + off.down_codes);
   const uint32_t *ds = reinterpret_cast<const uint32_t *>(rec + off.down_sb);
 #pragma unroll
@@ -658,45 +864,43 @@ __device__ __forceinline__ void down_load(const uint8_t *rec, const RecOffsets &
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = m.li + (j << m.lg);
-      if (valid && r < H && c < m.cpr) {
-        q[p][j] = *reinterpret_cast<const uint4 *>(dc + (size_t)r * m.wpr + (size_t)c * 4);
-        sb[p][j] = ds[(size_t)r * m.gpr + chunk_group<BITS>(c)];
-      } else {
-        q[p][j] = make_uint4(0, 0, 0, 0);
-        sb[p][j] = 0;
-      }
+      const bool in = r < H && c < m.cpr;
+      const int rr = in ? r : 0, cc = in ? c : 0;
+      t.q[p][j] = *reinterpret_cast<const uint4 *>(dc + (size_t)rr * m.wpr + (size_t)cc * 4);
+      t.sb[p][j] = ds[(size_t)rr * m.gpr + chunk_group<BITS>(cc)];
     }
   }
 }
 
-// weighted partial sums of one expert into acc[p]
-template <int BITS, int NCH, int NPASS>
-__device__ __forceinline__ void down_accumulate(const float *hin, const RowMap &m, bool valid,
-                                                float wgt, const uint4 (&q)[NPASS][NCH],
-                                                const uint32_t (&sb)[NPASS][NCH],
+// weighted partial sums of one expert into acc[p]; the passes are taken in
+// pairs so that two rows form independent accumulation chains
+template <int BITS, int NCH, int NPASS, int XS>
+__device__ __forceinline__ void down_accumulate(const float *hin, const RowMap &m, int H,
+                                                int row0, bool valid, float wgt,
+                                                const DnTile<BITS, NCH, NPASS> &t,
                                                 float (&acc)[NPASS]) {
   XStage<BITS, true> xs[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = m.li + (j << m.lg);
-    if (c < m.cpr) {
-      float v[ChunkGeom<BITS>::kCols];
-      load_x_chunk<BITS, XS_F32>(hin, nullptr, c * ChunkGeom<BITS>::kCols, v);
-      stage_chunk<BITS>(v, xs[j]);
-    }
+    xs[j] = make_stage<BITS, XS>(hin, hin, c < m.cpr ? c : 0);
   }
 #pragma unroll
-  for (int p = 0; p < NPASS; ++p) {
-    float part = 0.f;
+  for (int p = 0; p < NPASS; p += 2) {
+    constexpr int kLast = NPASS - 1;
+    const int p1 = p + 1 <= kLast ? p + 1 : p;
+    float part0 = 0.f, part1 = 0.f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int c = m.li + (j << m.lg);
-      if (c < m.cpr) {
-        const float d = chunk_dot<BITS>(q[p][j], xs[j]);
-        part = fmaf(bf_lo(sb[p][j]), d, fmaf(bf_hi(sb[p][j]), xs[j].xs, part));
-      }
+      const uint32_t s0 = in_tile(m, H, row0, p, j) ? t.sb[p][j] : 0u;
+      const uint32_t s1 = in_tile(m, H, row0, p1, j) ? t.sb[p1][j] : 0u;
+      float d0, d1;
+      chunk_dot2<BITS>(t.q[p][j], t.q[p1][j], xs[j], 0u, d0, d1);
+      part0 = fmaf(bf_lo(s0), d0, fmaf(bf_hi(s0), xs[j].xs, part0));
+      part1 = fmaf(bf_lo(s1), d1, fmaf(bf_hi(s1), xs[j].xs, part1));
     }
-    acc[p] = valid ? fmaf(wgt, part, acc[p]) : __builtin_nanf("");
+    acc[p] = valid ? fmaf(wgt, part0, acc[p]) : __builtin_nanf("");
+    if (p1 != p) acc[p1] = valid ? fmaf(wgt, part1, acc[p1]) : __builtin_nanf("");
   }
 }
 
@@ -706,12 +910,14 @@ __device__ __forceinline__ void down_accumulate(const float *hin, const RowMap &
 // (the reduction is linear).  SHARED_IN: the shared expert has the routed
 // width and is computed here; otherwise p.h_shared is null and p.y (if set)
 // holds its precomputed down output.
-template <int BITS, int NCH, int NPASS, int MAXK, bool SHARED_IN>
+template <int BITS, int NCH, int NPASS, int MAXK, bool SHARED_IN, bool USE_LDS>
 __global__ __launch_bounds__(kBlock) void k_down_combine(DownParams p) {
+  extern __shared__ float hl[];  // [K (+1)][I]: the SwiGLU outputs, staged once
+  constexpr int XSH = USE_LDS ? XS_NORM : XS_F32;
   const int wave = wave_uniform(blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6));
   const RowMap m = row_map<BITS>(p.I);
   const int row0 = wave * p.rows_per_wave;
-  if (row0 >= p.H) return;
+  const bool active = row0 < p.H;
 
   int ids[MAXK];
   float wk[MAXK];
@@ -720,17 +926,31 @@ __global__ __launch_bounds__(kBlock) void k_down_combine(DownParams p) {
     ids[k] = k < p.K ? wave_uniform(p.idx[k]) : -2;
     wk[k] = k < p.K ? p.w[k] : 0.f;
   }
-  uint4 q[MAXK][NPASS][NCH];
-  uint32_t sb[MAXK][NPASS][NCH];
+  // weight loads first, then h_routed [K][I] and h_shared [I] into LDS in
+  // one coalesced pass
+  DnTile<BITS, NCH, NPASS> t[MAXK];
 #pragma unroll
   for (int k = 0; k < MAXK; ++k) {
-    const bool v = k < p.K && ids[k] >= 0 && ids[k] < p.E;
-    down_load<BITS, NCH, NPASS>(p.experts + (size_t)(v ? ids[k] : 0) * p.stride, p.off, p.H, m,
-                                row0, v, q[k], sb[k]);
+    if (k < p.K) {  // wave-uniform
+      const bool v = ids[k] >= 0 && ids[k] < p.E;
+      down_load(t[k], p.experts + (size_t)(v ? ids[k] : 0) * p.stride, p.off, p.H, m, row0);
+    }
   }
-  uint4 qs[NPASS][NCH];
-  uint32_t sbs[NPASS][NCH];
-  if constexpr (SHARED_IN) down_load<BITS, NCH, NPASS>(p.shared_rec, p.soff, p.H, m, row0, true, qs, sbs);
+  DnTile<BITS, NCH, NPASS> ts;
+  if constexpr (SHARED_IN) down_load(ts, p.shared_rec, p.soff, p.H, m, row0);
+  if constexpr (USE_LDS) {
+    const int nh = (p.K + (SHARED_IN ? 1 : 0)) * p.I;
+    const int nr = p.K * p.I;
+    for (int e = threadIdx.x * 4; e < nh; e += kBlock * 4) {
+      const float4 v = e < nr ? *reinterpret_cast<const float4 *>(p.h_routed + e)
+                              : *reinterpret_cast<const float4 *>(p.h_shared + (e - nr));
+      *reinterpret_cast<float4 *>(hl + e) = v;
+    }
+    __syncthreads();
+  }
+  if (!active) return;
+  const float *hr = USE_LDS ? hl : p.h_routed;
+  const float *hs = USE_LDS ? hl + (size_t)p.K * p.I : p.h_shared;
 
   float acc[NPASS];
 #pragma unroll
@@ -739,11 +959,12 @@ __global__ __launch_bounds__(kBlock) void k_down_combine(DownParams p) {
   for (int k = 0; k < MAXK; ++k) {
     if (k < p.K) {
       const bool v = ids[k] >= 0 && ids[k] < p.E;
-      down_accumulate<BITS, NCH, NPASS>(p.h_routed + (size_t)k * p.I, m, v, wk[k], q[k], sb[k], acc);
+      down_accumulate<BITS, NCH, NPASS, XSH>(hr + (size_t)k * p.I, m, p.H, row0, v, wk[k], t[k], acc);
     }
   }
   const float sig = p.sigma[0];
-  if constexpr (SHARED_IN) down_accumulate<BITS, NCH, NPASS>(p.h_shared, m, true, sig, qs, sbs, acc);
+  if constexpr (SHARED_IN)
+    down_accumulate<BITS, NCH, NPASS, XSH>(hs, m, p.H, row0, true, sig, ts, acc);
 #pragma unroll
   for (int i = 0; i < NPASS; ++i) {
     const float s = seg_sum(acc[i], m.lg);
@@ -772,13 +993,12 @@ __global__ __launch_bounds__(kBlock) void k_down_y(DownParams p) {
   const bool shared = id == kSharedId;
   const bool valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
   const uint8_t *rec = shared ? p.shared_rec : p.experts + (size_t)(valid ? id : 0) * p.stride;
-  uint4 q[NPASS][NCH];
-  uint32_t sb[NPASS][NCH];
-  down_load<BITS, NCH, NPASS>(rec, shared ? p.soff : p.off, p.H, m, row0, valid, q, sb);
+  DnTile<BITS, NCH, NPASS> t;
+  down_load(t, rec, shared ? p.soff : p.off, p.H, m, row0);
   float acc[NPASS];
 #pragma unroll
   for (int i = 0; i < NPASS; ++i) acc[i] = 0.f;
-  down_accumulate<BITS, NCH, NPASS>(p.h + (size_t)slot * p.I, m, valid, 1.0f, q, sb, acc);
+  down_accumulate<BITS, NCH, NPASS, XS_F32>(p.h + (size_t)slot * p.I, m, p.H, row0, valid, 1.0f, t, acc);
 #pragma unroll
   for (int i = 0; i < NPASS; ++i) {
     const float s = seg_sum(acc[i], m.lg);
@@ -788,112 +1008,7 @@ __global__ __launch_bounds__(kBlock) void k_down_y(DownParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// elementwise combine (stand-alone entry point)
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_combine(CombineParams p) {
-  const int o = blockIdx.x * kBlock + threadIdx.x;
-  if (o >= p.H) return;
-  float acc = p.h_res[o];
-  for (int k = 0; k < p.K; ++k) acc = fmaf(p.w[k], p.y[(size_t)k * p.H + o], acc);
-  acc = fmaf(p.sigma[0], p.y_shared[o], acc);
-  p.out[o] = acc;
-}
-
-// ---------------------------------------------------------------------------
-// synthetic weights: SplitMix64 used counter-style (Steele, Lea and Flood,
-// OOPSLA 2014), see moe_fill_experts in include/moe.h
-// ---------------------------------------------------------------------------
-constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
-constexpr uint64_t kRoot = 0x6D6F652D67656E31ull;
-
-__device__ __forceinline__ uint64_t sm_mix(uint64_t z) {
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-__device__ __forceinline__ uint64_t sm_out(uint64_t key, uint64_t i) {
-  return sm_mix(key + (i + 1) * kGamma);
-}
-
-// fp64 -> bf16 bits, round to nearest even from the full significand
-__device__ __forceinline__ uint32_t f64_to_bf16(double v) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint32_t sign = (uint32_t)(b >> 63);
-  if ((b << 1) == 0) return sign << 15;
-  const int e = (int)((b >> 52) & 0x7FF);
-  const uint64_t m = (b & ((1ull << 52) - 1)) | (1ull << 52);
-  uint64_t keep = m >> 45;
-  const uint64_t rem = m & ((1ull << 45) - 1);
-  const uint64_t half = 1ull << 44;
-  if (rem > half || (rem == half && (keep & 1))) ++keep;
-  int exp = e - 1023 + 127;
-  if (keep == 256) {
-    keep = 128;
-    ++exp;
-  }
-  return (sign << 15) | ((uint32_t)exp << 7) | (uint32_t)(keep & 0x7F);
-}
-
-__device__ __forceinline__ uint32_t uniform_bf16(uint32_t u24, double lo, double hi) {
-  const double t = ((double)u24 + 0.5) * (1.0 / 16777216.0);
-  const double d = __dsub_rn(hi, lo);
-  const double v = __dadd_rn(lo, __dmul_rn(d, t));
-  return f64_to_bf16(v);
-}
-
-__global__ __launch_bounds__(kBlock) void k_fill(FillParams p) {
-  const int j = blockIdx.y;
-  uint8_t *rec = p.dst + (size_t)j * p.stride;
-  const uint64_t ng = (uint64_t)p.I * p.H * p.bits / 32;  // words of gate (= up)
-  const uint64_t nd = ng;                                  // words of down
-  const uint64_t gg = (uint64_t)p.I * (p.H / 64);          // sb words of gate (= up)
-  const uint64_t gd = (uint64_t)p.H * (p.I / 64);          // sb words of down
-  const uint64_t n_units[6] = {ng / 2, ng / 2, nd / 2, gg, gg, gd};
-  const size_t offs[6] = {p.off.gate_codes, p.off.up_codes, p.off.down_codes,
-                          p.off.gate_sb, p.off.up_sb, p.off.down_sb};
-  uint64_t base = sm_out(sm_out(sm_out(kRoot, p.seed), (uint64_t)p.layer),
-                         (uint64_t)(p.first_expert + j));
-  uint64_t total = 0;
-  for (int s = 0; s < 6; ++s) total += n_units[s];
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += stride) {
-    int s = 0;
-    uint64_t i = u;
-    while (i >= n_units[s]) {
-      i -= n_units[s];
-      ++s;
-    }
-    const uint64_t key = sm_out(base, (uint64_t)s);
-    const uint64_t r = sm_out(key, i);
-    if (s < 3) {
-      uint2 *dst = reinterpret_cast<uint2 *>(rec + offs[s]) + i;
-      *dst = make_uint2((uint32_t)r, (uint32_t)(r >> 32));
-    } else {
-      const uint32_t us = (uint32_t)(r >> 40);
-      const uint32_t ub = (uint32_t)((r >> 16) & 0xFFFFFFu);
-      const uint32_t sbits = uniform_bf16(us, p.scale_lo, p.scale_hi);
-      const uint32_t bbits = uniform_bf16(ub, p.bias_lo, p.bias_hi);
-      reinterpret_cast<uint32_t *>(rec + offs[s])[i] = sbits | (bbits << 16);
-    }
-  }
-}
-
-__global__ __launch_bounds__(kBlock) void k_zero(uint8_t *ptr, size_t bytes) {
-  const size_t n16 = bytes / 16;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-    reinterpret_cast<uint4 *>(ptr)[i] = make_uint4(0, 0, 0, 0);
-  const size_t tail = bytes - n16 * 16;
-  if (blockIdx.x == 0 && threadIdx.x < tail) ptr[n16 * 16 + threadIdx.x] = 0;
-}
-
-__global__ __launch_bounds__(kBlock) void k_copy_f32(float *dst, const float *src, int n) {
-  const int i = blockIdx.x * kBlock + threadIdx.x;
-  if (i < n) dst[i] = src[i];
-}
-
-// ---------------------------------------------------------------------------
-// launchers
+// launch shapes
 // ---------------------------------------------------------------------------
 static int nch_for(int cols, int bits) {
   const int cpr = cols * bits / 128;
@@ -908,38 +1023,75 @@ static int rpp_for(int cols, int bits) {
   return 64 >> lg;
 }
 
-#define MOE_DISPATCH_NCH(nch, ...) \
-  switch (nch) {                   \
-    case 1: { constexpr int NCH_ = 1; __VA_ARGS__; } break; \
-    case 2: { constexpr int NCH_ = 2; __VA_ARGS__; } break; \
-    default: { constexpr int NCH_ = 4; __VA_ARGS__; } break; \
-  }
+// Passes per wave (rows per wave = passes * rows per pass) of each kernel.
+// MOE_TUNE="gu=<p>,dn=<p>,sh=<p>" (p = 1, 2 or 4) overrides the defaults.
+struct Tune {
+  int gu = 0, dn = 0, sh = 0;
+};
+static const Tune &tune() {
+  static const Tune t = [] {
+    Tune r;
+    const char *e = getenv("MOE_TUNE");
+    if (!e) return r;
+    for (const char *s = e; *s;) {
+      int v = 0;
+      if (sscanf(s, "gu=%d", &v) == 1) r.gu = v;
+      else if (sscanf(s, "dn=%d", &v) == 1) r.dn = v;
+      else if (sscanf(s, "sh=%d", &v) == 1) r.sh = v;
+      while (*s && *s != ',') ++s;
+      if (*s == ',') ++s;
+    }
+    return r;
+  }();
+  return t;
+}
+static int pick_pass(int tuned, int dflt) {
+  return (tuned == 1 || tuned == 2 || tuned == 4) ? tuned : dflt;
+}
 
-// rows of the shared expert per wave in K1
-constexpr int kHeadSharedPass = 2;
+// instantiated (NCH, NPASS) pairs; NCH 4 (rows wider than 2048 codes per
+// 64 lanes) only with one pass
+#define MOE_DISPATCH(nch, npass, ...)                                                    \
+  do {                                                                                   \
+    if (nch == 1 && npass == 1) { constexpr int NCH_ = 1, NP_ = 1; __VA_ARGS__; }        \
+    else if (nch == 1 && npass == 2) { constexpr int NCH_ = 1, NP_ = 2; __VA_ARGS__; }   \
+    else if (nch == 1) { constexpr int NCH_ = 1, NP_ = 4; __VA_ARGS__; }                 \
+    else if (nch == 2 && npass == 1) { constexpr int NCH_ = 2, NP_ = 1; __VA_ARGS__; }   \
+    else if (nch == 2 && npass == 2) { constexpr int NCH_ = 2, NP_ = 2; __VA_ARGS__; }   \
+    else if (nch == 2) { constexpr int NCH_ = 2, NP_ = 4; __VA_ARGS__; }                 \
+    else { constexpr int NCH_ = 4, NP_ = 1; __VA_ARGS__; }                              \
+  } while (0)
+
+static int clamp_pass(int nch, int npass) { return nch >= 4 ? 1 : npass; }
+
+size_t xstage_pair_bytes(int cols, int bits) {
+  return (size_t)(cols * bits / 128) * (64 / bits) * 4;
+}
+size_t xstage_sum_bytes(int cols, int bits) { return (size_t)(cols * bits / 128) * 8; }
 
 hipError_t launch_head(const HeadParams &p0, hipStream_t s) {
   HeadParams p = p0;
-  if (p.n_shared_waves > 0) {  // size the shared-expert part of the grid
-    p.shared_rows_per_wave = kHeadSharedPass * rpp_for(p.H, p.bits_shared);
-    p.n_shared_waves = (p.I + p.shared_rows_per_wave - 1) / p.shared_rows_per_wave;
-  }
-  const int rows = p.E + 1;
-  p.n_router_blocks = (p.T * rows + 3) / 4;
-  const int nsb = p.n_shared_waves > 0 ? (p.n_shared_waves + 3) / 4 : 0;
-  const dim3 grid(p.n_router_blocks + nsb);
-  const size_t lds = p.xsrc == XS_NORM ? (size_t)p.H * sizeof(float) : 0;
   const int bs = p.n_shared_waves > 0 ? p.bits_shared : 0;
   const int nch = bs ? nch_for(p.H, bs) : 1;
-#define MOE_HEAD(XS)                                                                         \
-  if (bs == 4) {                                                                             \
-    MOE_DISPATCH_NCH(nch, hipLaunchKernelGGL((k_head<XS, 4, NCH_, kHeadSharedPass>), grid,   \
-                                             dim3(kBlock), lds, s, p));                      \
-  } else if (bs == 2) {                                                                      \
-    MOE_DISPATCH_NCH(nch, hipLaunchKernelGGL((k_head<XS, 2, NCH_, kHeadSharedPass>), grid,   \
-                                             dim3(kBlock), lds, s, p));                      \
-  } else {                                                                                   \
-    hipLaunchKernelGGL((k_head<XS, 0, 1, 1>), grid, dim3(kBlock), lds, s, p);                \
+  const int npass = bs ? clamp_pass(nch, pick_pass(tune().sh, 2)) : 1;
+  if (bs) {  // size the shared-expert part of the grid
+    p.shared_rows_per_wave = npass * rpp_for(p.H, bs);
+    p.n_shared_waves = (p.I + p.shared_rows_per_wave - 1) / p.shared_rows_per_wave;
+  }
+  const int units = p.T * (p.E + 1) + 1;  // rows of every token, then the x stager
+  p.n_router_blocks = (units + 3) / 4;
+  const int nsb = bs ? (p.n_shared_waves + 3) / 4 : 0;
+  const dim3 grid(p.n_router_blocks + nsb);
+  const size_t lds = p.xsrc == XS_NORM ? (size_t)p.H * sizeof(float) : 0;
+#define MOE_HEAD(XS)                                                                             \
+  if (bs == 4) {                                                                                 \
+    MOE_DISPATCH(nch, npass,                                                                     \
+                 hipLaunchKernelGGL((k_head<XS, 4, NCH_, NP_>), grid, dim3(kBlock), lds, s, p)); \
+  } else if (bs == 2) {                                                                          \
+    MOE_DISPATCH(nch, npass,                                                                     \
+                 hipLaunchKernelGGL((k_head<XS, 2, NCH_, NP_>), grid, dim3(kBlock), lds, s, p)); \
+  } else {                                                                                       \
+    hipLaunchKernelGGL((k_head<XS, 0, 1, 1>), grid, dim3(kBlock), lds, s, p);                    \
   }
   if (p.xsrc == XS_BF16) {
     MOE_HEAD(XS_BF16)
@@ -953,7 +1105,7 @@ hipError_t launch_head(const HeadParams &p0, hipStream_t s) {
 }
 
 hipError_t launch_topk(const TopkParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(p.T), dim3(64), 0, s, p);
+  hipLaunchKernelGGL(k_topk, dim3(p.T), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
@@ -961,24 +1113,19 @@ hipError_t launch_gateup(const GateUpParams &p0, hipStream_t s) {
   GateUpParams p = p0;
   const int nch = nch_for(p.H, p.bits);
   const int rpp = rpp_for(p.H, p.bits);
-  // about four rows per wave on wide rows, one pass on packed short rows
-  const int npass = rpp >= 4 ? 1 : (p.I >= 4 * 64 ? 4 : 2);
+  const int npass = clamp_pass(nch, pick_pass(tune().gu, rpp >= 4 ? 1 : 2));
   p.rows_per_wave = npass * rpp;
   p.waves_per_expert = (p.I + p.rows_per_wave - 1) / p.rows_per_wave;
+  p.n_shared_blocks = p.with_shared ? (p.waves_per_expert + 3) / 4 : 0;
   const int waves = p.waves_per_expert * p.n;
-  const dim3 grid((waves + 3) / 4);
-#define MOE_GU(BITS, XS)                                                                        \
-  MOE_DISPATCH_NCH(nch, if (npass == 1) {                                                      \
-    hipLaunchKernelGGL((k_gateup<BITS, NCH_, 1, XS>), grid, dim3(kBlock), 0, s, p);            \
-  } else if (npass == 2) {                                                                     \
-    hipLaunchKernelGGL((k_gateup<BITS, NCH_, 2, XS>), grid, dim3(kBlock), 0, s, p);            \
-  } else {                                                                                     \
-    hipLaunchKernelGGL((k_gateup<BITS, NCH_, 4, XS>), grid, dim3(kBlock), 0, s, p);            \
-  })
+  const dim3 grid(p.n_shared_blocks + (waves + 3) / 4);
+#define MOE_GU(BITS, XS)                                                                    \
+  MOE_DISPATCH(nch, npass, hipLaunchKernelGGL((k_gateup<BITS, NCH_, NP_, XS>), grid,         \
+                                              dim3(kBlock), 0, s, p))
   if (p.bits == 4) {
-    if (p.xsrc == XS_BF16) { MOE_GU(4, XS_BF16) } else { MOE_GU(4, XS_F32) }
+    if (p.xsrc == XS_BF16) { MOE_GU(4, XS_BF16); } else { MOE_GU(4, XS_F32); }
   } else {
-    if (p.xsrc == XS_BF16) { MOE_GU(2, XS_BF16) } else { MOE_GU(2, XS_F32) }
+    if (p.xsrc == XS_BF16) { MOE_GU(2, XS_BF16); } else { MOE_GU(2, XS_F32); }
   }
 #undef MOE_GU
   return hipGetLastError();
@@ -989,73 +1136,44 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
   const int bits = p.bits_r;
   const int nch = nch_for(p.I, bits);
   const int rpp = rpp_for(p.I, bits);
-  const int npass = rpp >= 8 ? 1 : 2;
+  const int npass = clamp_pass(nch, pick_pass(tune().dn, rpp >= 8 ? 1 : 2));
   p.rows_per_wave = npass * rpp;
   if (p.combine) {
     const bool shared_in = p.h_shared != nullptr;
     const int waves = (p.H + p.rows_per_wave - 1) / p.rows_per_wave;
     const dim3 grid((waves + 3) / 4);
-    const int maxk = p.K <= 2 ? 2 : (p.K <= 4 ? 4 : 8);
-#define MOE_DC(BITS, MAXK, SIN)                                                                  \
-  MOE_DISPATCH_NCH(nch, if (npass == 1) {                                                       \
-    hipLaunchKernelGGL((k_down_combine<BITS, NCH_, 1, MAXK, SIN>), grid, dim3(kBlock), 0, s, p); \
-  } else {                                                                                      \
-    hipLaunchKernelGGL((k_down_combine<BITS, NCH_, 2, MAXK, SIN>), grid, dim3(kBlock), 0, s, p); \
-  })
-#define MOE_DC_K(BITS, SIN)        \
-  if (maxk == 2) {                 \
-    MOE_DC(BITS, 2, SIN)           \
-  } else if (maxk == 4) {          \
-    MOE_DC(BITS, 4, SIN)           \
-  } else {                         \
-    MOE_DC(BITS, 8, SIN)           \
-  }
+    const bool k4 = p.K <= 4;
+    // the SwiGLU outputs go through LDS when they fit in 64 KiB
+    const size_t hbytes = (size_t)(p.K + (shared_in ? 1 : 0)) * p.I * sizeof(float);
+    const bool use_lds = hbytes <= 65536;
+    const size_t lds = use_lds ? hbytes : 0;
+#define MOE_DC(BITS, MAXK, SIN)                                                                   \
+  do {                                                                                            \
+    if (use_lds)                                                                                  \
+      MOE_DISPATCH(nch, npass, hipLaunchKernelGGL((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, true>), \
+                                                  grid, dim3(kBlock), lds, s, p));                \
+    else                                                                                          \
+      MOE_DISPATCH(nch, npass, hipLaunchKernelGGL((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, false>), \
+                                                  grid, dim3(kBlock), 0, s, p));                  \
+  } while (0)
     if (bits == 4) {
-      if (shared_in) { MOE_DC_K(4, true) } else { MOE_DC_K(4, false) }
+      if (shared_in) { if (k4) MOE_DC(4, 4, true); else MOE_DC(4, 8, true); }
+      else { if (k4) MOE_DC(4, 4, false); else MOE_DC(4, 8, false); }
     } else {
-      if (shared_in) { MOE_DC_K(2, true) } else { MOE_DC_K(2, false) }
+      if (shared_in) { if (k4) MOE_DC(2, 4, true); else MOE_DC(2, 8, true); }
+      else { if (k4) MOE_DC(2, 4, false); else MOE_DC(2, 8, false); }
     }
-#undef MOE_DC_K
 #undef MOE_DC
   } else {
     p.waves_per_expert = (p.H + p.rows_per_wave - 1) / p.rows_per_wave;
     const int waves = p.waves_per_expert * p.n;
     const dim3 grid((waves + 3) / 4);
-#define MOE_DY(BITS)                                                                  \
-  MOE_DISPATCH_NCH(nch, if (npass == 1) {                                            \
-    hipLaunchKernelGGL((k_down_y<BITS, NCH_, 1>), grid, dim3(kBlock), 0, s, p);      \
-  } else {                                                                           \
-    hipLaunchKernelGGL((k_down_y<BITS, NCH_, 2>), grid, dim3(kBlock), 0, s, p);      \
-  })
-    if (bits == 4) { MOE_DY(4) } else { MOE_DY(2) }
+#define MOE_DY(BITS)                                                                           \
+  MOE_DISPATCH(nch, npass, hipLaunchKernelGGL((k_down_y<BITS, NCH_, NP_>), grid, dim3(kBlock),  \
+                                              0, s, p))
+    if (bits == 4) { MOE_DY(4); } else { MOE_DY(2); }
 #undef MOE_DY
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_combine(const CombineParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3((p.H + kBlock - 1) / kBlock), dim3(kBlock), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill(const FillParams &p, hipStream_t s) {
-  const dim3 grid(1024, p.n);
-  hipLaunchKernelGGL(k_fill, grid, dim3(kBlock), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t s) {
-  if (bytes == 0) return hipSuccess;
-  size_t blocks = (bytes / 16 + kBlock - 1) / kBlock;
-  if (blocks < 1) blocks = 1;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(kBlock), 0, s,
-                     static_cast<uint8_t *>(ptr), bytes);
-  return hipGetLastError();
-}
-
-hipError_t launch_copy_f32(float *dst, const float *src, int n, hipStream_t s) {
-  hipLaunchKernelGGL(k_copy_f32, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, dst, src, n);
   return hipGetLastError();
 }
 

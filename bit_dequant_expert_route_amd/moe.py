@@ -77,6 +77,8 @@ def _load():
         "moe_fill_experts": (I, [P, Z, I, C.c_uint64, I, I, I, I, I, C.c_double, C.c_double,
                                  C.c_double, C.c_double, P]),
         "moe_zero": (I, [P, Z, P]),
+        "moe_profile_begin": (I, [I]),
+        "moe_profile_end": (I, [C.POINTER(C.c_float), C.POINTER(C.c_int), I, C.POINTER(C.c_int)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -289,6 +291,23 @@ def fill_experts(dst, stride: int, n: int, seed: int, layer: int, first_expert: 
                                  hidden, inter, bits, dist.scale_lo, dist.scale_hi,
                                  dist.bias_lo, dist.bias_hi, _stream(stream)),
            "moe_fill_experts")
+
+
+KERNEL_NAMES = {1: "head", 2: "gateup", 3: "down_combine", 4: "down_y", 5: "topk",
+                6: "combine", 7: "other"}
+
+
+def profile_begin(max_launches: int):
+    _check(_lib.moe_profile_begin(max_launches), "moe_profile_begin")
+
+
+def profile_end(capacity: int):
+    """[(kernel name, ms), ...] of the launches recorded since profile_begin."""
+    ms = (C.c_float * capacity)()
+    ids = (C.c_int * capacity)()
+    n = C.c_int(0)
+    _check(_lib.moe_profile_end(ms, ids, capacity, C.byref(n)), "moe_profile_end")
+    return [(KERNEL_NAMES.get(ids[i], str(ids[i])), float(ms[i])) for i in range(n.value)]
 
 
 def zero(t, stream=None):

@@ -34,7 +34,8 @@
  *     multiples of 64 in [64, 8192]; 1 <= top_k <= 8, top_k <= n_experts <=
  *     1024; 1 <= n_tokens <= 64.  Alignment: records, expert_stride and the
  *     workspace on 256 bytes, every other vector on 16 bytes (MOE_EALIGN).
- *   - Reentrant: the only global state is the thread-local error string.
+ *   - Reentrant: the only global state is thread-local (the error string and
+ *     the kernel-timing switch of moe_profile_begin).
  *
  * Record format (one expert, `moe_expert_bytes` bytes, sections on 256-byte
  * boundaries, in this order):
@@ -216,6 +217,30 @@ int moe_graph_create_stack(const moe_layer_t *layers, int n_layers,
                            moe_graph_t *out);
 int moe_graph_launch(moe_graph_t g, void *stream);
 int moe_graph_destroy(moe_graph_t g);
+
+/* ---------------------------------------------------------------------- */
+/* kernel timing                                                            */
+/* ---------------------------------------------------------------------- */
+/* Kernels the library launches, as reported by moe_profile_end. */
+enum {
+    MOE_KERNEL_HEAD = 1,       /* router rows + shared gate + shared gate/up */
+    MOE_KERNEL_GATEUP = 2,     /* routed gate/up + SwiGLU (with top-K) */
+    MOE_KERNEL_DOWN = 3,       /* down projections + combine + residual */
+    MOE_KERNEL_DOWN_Y = 4,     /* down projection writing per-expert y */
+    MOE_KERNEL_TOPK = 5,
+    MOE_KERNEL_COMBINE = 6,
+    MOE_KERNEL_OTHER = 7
+};
+/* Between moe_profile_begin and moe_profile_end, on the calling thread, every
+ * kernel launch of the path entry points is bracketed by two HIP events on
+ * its stream (not while the stream is being captured into a graph).  Up to
+ * max_launches launches are recorded; later ones are not.  The events are
+ * created here and destroyed by moe_profile_end. */
+int moe_profile_begin(int max_launches);
+/* Wait for the recorded launches and write, in launch order, the elapsed
+ * milliseconds between each launch's two events (ms[i]) and its kernel id
+ * (kernel_ids[i], may be NULL); *n_out receives the number written. */
+int moe_profile_end(float *ms, int *kernel_ids, int capacity, int *n_out);
 
 /* ---------------------------------------------------------------------- */
 /* synthetic weights                                                        */
