@@ -462,117 +462,107 @@ __device__ __forceinline__ void gu_compute(const GUTile<BITS, NCH, NPASS> &t,
 }
 
 // ---------------------------------------------------------------------------
-// top-K of E logits by one workgroup: K selection rounds of an arg-max (ties
-// to the lower index), then the softmax weights of the selected experts
-// ([openclawradar] "Pipeline performance": softmax + topK routing)
+// top-K of E logits by one wave: K rounds of (wave maximum, lowest index that
+// holds it), then the softmax weights of the selected experts
+// ([openclawradar] "Pipeline performance": softmax + topK routing).
+// Lane l holds experts e = 64 i + l, so each load is one coalesced row.  A
+// selected (or absent) entry becomes NaN, which the maximum skips; a NaN
+// logit is never selected.
 // ---------------------------------------------------------------------------
-struct TopKShared {
-  int idx[kMaxK];
-  float w[kMaxK];
-  float rv[kBlock / 64];
-  int re[kBlock / 64];
-  float z[kBlock / 64];
-};
+constexpr int kTopkNpl = kMaxE / 64;
 
-__device__ __forceinline__ void argmax_merge(float &v, int &e, float ov, int oe) {
-  if (ov > v || (ov == v && oe < e)) {
-    v = ov;
-    e = oe;
-  }
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  // every lane of each 16-lane row now holds its row's maximum
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
-// arg-max over the wave; the result is returned in every lane
-__device__ __forceinline__ void wave_argmax(float &v, int &e) {
-  argmax_merge(v, e, dpp<0xB1>(v), dpp_i<0xB1>(e));
-  argmax_merge(v, e, dpp<0x4E>(v), dpp_i<0x4E>(e));
-  argmax_merge(v, e, dpp<0x141>(v), dpp_i<0x141>(e));
-  argmax_merge(v, e, dpp<0x140>(v), dpp_i<0x140>(e));
-  // every lane of each 16-lane row now holds its row's best
-  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  int be = __builtin_amdgcn_readlane(e, 0);
+// the logits of one token, one register per 64 experts
+__device__ __forceinline__ void topk_load(const float *__restrict__ lg, int E,
+                                          float (&v)[kTopkNpl]) {
+  const int lane = lane_id();
 #pragma unroll
-  for (int r = 1; r < 4; ++r)
-    argmax_merge(bv, be, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r)),
-                 __builtin_amdgcn_readlane(e, 16 * r));
-  v = bv;
-  e = be;
-}
-
-// every thread of the (256-thread) workgroup must call this
-__device__ void block_topk(const float *__restrict__ lg, int E, int K, int renorm,
-                           TopKShared &sh) {
-  constexpr int NV = kMaxE / kBlock;
-  constexpr int kNone = 0x7fffffff;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  float v[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = tid + kBlock * i;
-    v[i] = e < E ? lg[e] : -INFINITY;
-  }
-  uint32_t taken = 0;
-  float lk[kMaxK];
-  int ik[kMaxK];
-#pragma unroll
-  for (int k = 0; k < kMaxK; ++k) {
-    lk[k] = -INFINITY;
-    ik[k] = kNone;
-    if (k < K) {
-      float bv = -INFINITY;
-      int be = kNone;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int e = tid + kBlock * i;
-        if (e < E && !((taken >> i) & 1u)) argmax_merge(bv, be, v[i], e);
-      }
-      wave_argmax(bv, be);
-      if (lane == 0) {
-        sh.rv[wv] = bv;
-        sh.re[wv] = be;
-      }
-      __syncthreads();
-      bv = sh.rv[0];
-      be = sh.re[0];
-#pragma unroll
-      for (int w = 1; w < kBlock / 64; ++w) argmax_merge(bv, be, sh.rv[w], sh.re[w]);
-      __syncthreads();
-      if (be != kNone && (be % kBlock) == tid) taken |= 1u << (be / kBlock);
-      lk[k] = bv;
-      ik[k] = be;
+  for (int i = 0; i < kTopkNpl; ++i) {
+    const int e = i * 64 + lane;
+    v[i] = __builtin_nanf("");
+    if (i * 64 < E) {  // wave-uniform
+      // canonical values let the maxima below skip their NaN quieting
+      const float l = __builtin_canonicalizef(lg[e < E ? e : 0]);
+      v[i] = e < E ? l : __builtin_nanf("");
     }
   }
-  const float mx = lk[0];
-  float den;
-  if (renorm) {
-    den = 0.f;
+}
+
+// Selection on the loaded logits, of which the first NPL registers hold
+// experts (the others are NaN).  Lane k < K comes back with the k-th selected
+// expert (descending logit; -2 if fewer than k+1 logits are numbers) in e_out
+// and its weight in w_out; the other lanes get -2 and NaN.
+template <int NPL>
+__device__ __forceinline__ void topk_select_n(float (&v)[kTopkNpl], int K, int renorm,
+                                              int &e_out, float &w_out) {
+  const int lane = lane_id();
+  float my_l = __builtin_nanf("");
+  int my_e = -2;
+  float mx = __builtin_nanf("");
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    float m = v[0];
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k)
-      if (k < K) den += expf(lk[k] - mx);
-  } else {
-    float z = 0.f;
+    for (int i = 1; i < NPL; ++i) m = fmaxf(m, v[i]);
+    m = wave_max(m);
+    // lowest expert index that holds the maximum
+    int sel = -2;
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (tid + kBlock * i < E) z += expf(v[i] - mx);
-    z = seg_sum(z, 6);
-    if (lane == 0) sh.z[wv] = z;
-    __syncthreads();
-    den = 0.f;
+    for (int i = NPL - 1; i >= 0; --i) {
+      const uint64_t b = __ballot(v[i] == m);
+      if (b) sel = i * 64 + __builtin_ctzll(b);
+    }
+    sel = wave_uniform(sel);
+    const int si = sel >> 6, sl = sel & 63;  // sel < 0 matches no lane
 #pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) den += sh.z[w];
+    for (int i = 0; i < NPL; ++i)
+      if (i == si && lane == sl) v[i] = __builtin_nanf("");
+    if (lane == k) {
+      my_l = m;
+      my_e = sel;
+    }
+    if (k == 0) mx = m;
   }
-  if (tid < K) {
-    int e = kNone;
-    float l = -INFINITY;
+  const bool mine = lane < K && my_e >= 0;
+  const float t = mine ? expf(my_l - mx) : 0.f;
+  float z = t;
+  if (!renorm) {
+    // the unselected experts join the denominator
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k)
-      if (k == tid) {
-        e = ik[k];
-        l = lk[k];
-      }
-    sh.idx[tid] = e == kNone ? -2 : e;
-    sh.w[tid] = e == kNone ? __builtin_nanf("") : expf(l - mx) / den;
+    for (int i = 0; i < NPL; ++i)
+      if (!__builtin_isnan(v[i])) z += expf(v[i] - mx);
   }
-  __syncthreads();
+  const float den = seg_sum(z, 6);
+  e_out = my_e;
+  w_out = mine ? t / den : __builtin_nanf("");
+}
+
+__device__ __forceinline__ void topk_select(float (&v)[kTopkNpl], int E, int K, int renorm,
+                                            int &e_out, float &w_out) {
+  static_assert(kTopkNpl == 16, "two register counts below");
+  if (E <= 512) topk_select_n<8>(v, K, renorm, e_out, w_out);
+  else topk_select_n<16>(v, K, renorm, e_out, w_out);
+}
+
+// lanes 0..K-1 write the selection
+__device__ __forceinline__ void topk_store(int e, float w, int K, int32_t *idx, float *wout) {
+  const int lane = lane_id();
+  if (lane < K) {
+    if (idx) idx[lane] = e;
+    if (wout) wout[lane] = w;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -760,16 +750,16 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// stand-alone top-K (one workgroup per token)
+// stand-alone top-K (one wave per token)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_topk(TopkParams p) {
-  __shared__ TopKShared sh;
+__global__ __launch_bounds__(64) void k_topk(TopkParams p) {
   const int t = blockIdx.x;
-  block_topk(p.logits + (size_t)t * p.E, p.E, p.K, p.renorm, sh);
-  if ((int)threadIdx.x < p.K) {
-    p.idx[(size_t)t * p.K + threadIdx.x] = sh.idx[threadIdx.x];
-    p.w[(size_t)t * p.K + threadIdx.x] = sh.w[threadIdx.x];
-  }
+  float v[kTopkNpl];
+  topk_load(p.logits + (size_t)t * p.E, p.E, v);
+  int e;
+  float w;
+  topk_select(v, p.E, p.K, p.renorm, e, w);
+  topk_store(e, w, p.K, p.idx + (size_t)t * p.K, p.w + (size_t)t * p.K);
 }
 
 // ---------------------------------------------------------------------------
@@ -778,41 +768,28 @@ __global__ __launch_bounds__(kBlock) void k_topk(TopkParams p) {
 // ---------------------------------------------------------------------------
 template <int BITS, int NCH, int NPASS, int XS>
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
-  __shared__ TopKShared sh;
+  __shared__ int sel_ids[kMaxK];
   const int blk = wave_uniform(blockIdx.x);
   const int wv = wave_uniform(threadIdx.x >> 6);
-  int id, wie;
-  float *hout;
-  if (blk < p.n_shared_blocks) {
-    // the shared expert does not depend on the routing: these workgroups
-    // stream its rows while the routed ones are still selecting experts
-    wie = blk * (kBlock / 64) + wv;
-    if (wie >= p.waves_per_expert) return;
-    id = kSharedId;
-    hout = p.h_shared_out;
-  } else {
-    const int wave = (blk - p.n_shared_blocks) * (kBlock / 64) + wv;
-    if (!p.ids) {
-      block_topk(p.logits, p.E, p.K, p.renorm, sh);
-      if (blk == p.n_shared_blocks && (int)threadIdx.x < p.K) {
-        if (p.idx_out) p.idx_out[threadIdx.x] = sh.idx[threadIdx.x];
-        if (p.w_out) p.w_out[threadIdx.x] = sh.w[threadIdx.x];
-      }
-    }
-    const int slot = wave / p.waves_per_expert;
-    if (slot >= p.n) return;
-    wie = wave - slot * p.waves_per_expert;
-    id = wave_uniform(p.ids ? p.ids[slot] : sh.idx[slot]);
-    hout = p.h_out + (size_t)slot * p.I;
-  }
-  const bool shared = id == kSharedId;
-  const bool valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
-  const uint8_t *rec = shared ? p.shared_rec : p.experts + (size_t)(valid ? id : 0) * p.stride;
+  const bool shared_blk = blk < p.n_shared_blocks;
+  // the shared expert does not depend on the routing: its workgroups come
+  // first and stream its rows while the routed ones are selecting experts
+  const int wave = shared_blk ? blk * (kBlock / 64) + wv
+                              : (blk - p.n_shared_blocks) * (kBlock / 64) + wv;
+  const int slot = shared_blk ? 0 : wave / p.waves_per_expert;
+  const int wie = shared_blk ? wave : wave - slot * p.waves_per_expert;
+  const bool topk = !shared_blk && !p.ids;  // workgroup-uniform
+  if (!topk && (shared_blk ? wie >= p.waves_per_expert : slot >= p.n)) return;
+
+  // Routing: wave 0 of the workgroup loads the logits and selects, the
+  // others wait at one barrier (one selection per workgroup, not per wave).
+  // Loads go out in the order they are needed (vmcnt counts in order):
+  // logits, x, then the weights once the expert is known.
+  float lv[kTopkNpl];
+  if (topk && wv == 0) topk_load(p.logits, p.E, lv);
   constexpr bool XF32 = XS != XS_BF16;
   const RowMap m = row_map<BITS>(p.H);
   const int row0 = wie * p.rows_per_wave;
-  // x loads first, then the weight loads, then the staging math: vmcnt is in
-  // order, so the staging waits only for x
   XStage<BITS, XF32> xs[NCH];
   XRaw<BITS, XS> xr[NCH];
   bool from_buf = false;
@@ -833,6 +810,32 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+
+  int id;
+  float *hout;
+  if (shared_blk) {
+    id = kSharedId;
+    hout = p.h_shared_out;
+  } else {
+    if (topk) {
+      if (wv == 0) {
+        int e;
+        float w;
+        topk_select(lv, p.E, p.K, p.renorm, e, w);
+        if (blk == p.n_shared_blocks) topk_store(e, w, p.K, p.idx_out, p.w_out);
+        if (lane_id() < p.K) sel_ids[lane_id()] = e;
+      }
+      __syncthreads();
+      if (slot >= p.n) return;
+      id = wave_uniform(sel_ids[slot]);
+    } else {
+      id = wave_uniform(p.ids[slot]);
+    }
+    hout = p.h_out + (size_t)slot * p.I;
+  }
+  const bool shared = id == kSharedId;
+  const bool valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
+  const uint8_t *rec = shared ? p.shared_rec : p.experts + (size_t)(valid ? id : 0) * p.stride;
   GUTile<BITS, NCH, NPASS> tile;
   gu_load(tile, rec, shared ? p.soff : p.off, m, p.I, row0);
   __builtin_amdgcn_sched_barrier(0);
@@ -1105,7 +1108,7 @@ hipError_t launch_head(const HeadParams &p0, hipStream_t s) {
 }
 
 hipError_t launch_topk(const TopkParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(p.T), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL(k_topk, dim3(p.T), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
