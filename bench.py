@@ -11,9 +11,10 @@ activation per instance over one 512-expert pool, 5 GB touched per replay), so
 that no layer's weights are still in the 256 MB Infinity Cache when it runs.
 `value` is the decode latency of one layer = step time / R.
 
-Also reported: per-kernel durations measured with HIP events around each launch
-(the library's timing hook), the roofline of the dominant kernel (routed
-gate/up), and the fp64 CPU oracle timed on a bounded sample on the host.
+Also reported: per-kernel durations from HIP events that each kernel's dispatch
+records itself (the library's timing hook, one eager pass over the rotation
+set), the roofline of the dominant kernel (shared + routed gate/up), and the
+fp64 CPU oracle timed on a bounded sample on the host.
 """
 from __future__ import annotations
 
@@ -208,7 +209,7 @@ def main():
     ms_per_step = e0.elapsed_time(e1) / args.steps
     us_per_layer = ms_per_step * 1000.0 / R
 
-    # per-kernel durations (HIP events around each launch, eager launches)
+    # per-kernel durations (events recorded by each dispatch, eager launches)
     n_launch = args.profile_passes * R * 4
     moe.profile_begin(n_launch)
     for _ in range(args.profile_passes):

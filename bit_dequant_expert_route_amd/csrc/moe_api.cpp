@@ -54,16 +54,15 @@ bool prof_active(hipStream_t s) {
   return true;
 }
 
-// launch `fn` with events around it when profiling
+// launch `fn` (one kernel) so that its dispatch records a pair of events
 template <class F>
 hipError_t timed(hipStream_t s, int id, F &&fn) {
   if (!prof_active(s)) return fn();
   const int i = g_prof.n;
-  hipError_t e = hipEventRecord(g_prof.ev[2 * i], s);
-  if (e != hipSuccess) return e;
-  e = fn();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(g_prof.ev[2 * i + 1], s);
+  g_launch_events.start = g_prof.ev[2 * i];
+  g_launch_events.stop = g_prof.ev[2 * i + 1];
+  const hipError_t e = fn();
+  g_launch_events = LaunchEvents{};
   if (e != hipSuccess) return e;
   g_prof.ids[i] = id;
   g_prof.n = i + 1;

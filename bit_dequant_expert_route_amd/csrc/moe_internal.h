@@ -2,6 +2,7 @@
 // (moe_api.cpp) and the gfx950 kernels (moe_kernels.hip).  Library-internal.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -160,6 +161,23 @@ struct FillParams {
 hipError_t launch_fill(const FillParams &p, hipStream_t s);
 
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t s);
+
+// Kernel timing: while `start` is set, each launcher's kernel dispatch records
+// these two events itself (the dispatch packet's own begin and end), so the
+// elapsed time is the kernel's execution time with no marker packets around it.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchEvents g_launch_events;
+
+#define MOE_LAUNCH(kern, grid, block, lds, stream, ...)                                      \
+  do {                                                                                       \
+    if (::moe_impl::g_launch_events.start)                                                   \
+      hipExtLaunchKernelGGL(kern, grid, block, lds, stream, ::moe_impl::g_launch_events.start, \
+                            ::moe_impl::g_launch_events.stop, 0, __VA_ARGS__);               \
+    else                                                                                     \
+      hipLaunchKernelGGL(kern, grid, block, lds, stream, __VA_ARGS__);                       \
+  } while (0)
 
 // bytes of the staged-x buffers for a row of `cols` columns at `bits`
 size_t xstage_pair_bytes(int cols, int bits);

@@ -1089,12 +1089,12 @@ hipError_t launch_head(const HeadParams &p0, hipStream_t s) {
 #define MOE_HEAD(XS)                                                                             \
   if (bs == 4) {                                                                                 \
     MOE_DISPATCH(nch, npass,                                                                     \
-                 hipLaunchKernelGGL((k_head<XS, 4, NCH_, NP_>), grid, dim3(kBlock), lds, s, p)); \
+                 MOE_LAUNCH((k_head<XS, 4, NCH_, NP_>), grid, dim3(kBlock), lds, s, p)); \
   } else if (bs == 2) {                                                                          \
     MOE_DISPATCH(nch, npass,                                                                     \
-                 hipLaunchKernelGGL((k_head<XS, 2, NCH_, NP_>), grid, dim3(kBlock), lds, s, p)); \
+                 MOE_LAUNCH((k_head<XS, 2, NCH_, NP_>), grid, dim3(kBlock), lds, s, p)); \
   } else {                                                                                       \
-    hipLaunchKernelGGL((k_head<XS, 0, 1, 1>), grid, dim3(kBlock), lds, s, p);                    \
+    MOE_LAUNCH((k_head<XS, 0, 1, 1>), grid, dim3(kBlock), lds, s, p);                    \
   }
   if (p.xsrc == XS_BF16) {
     MOE_HEAD(XS_BF16)
@@ -1108,7 +1108,7 @@ hipError_t launch_head(const HeadParams &p0, hipStream_t s) {
 }
 
 hipError_t launch_topk(const TopkParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(p.T), dim3(64), 0, s, p);
+  MOE_LAUNCH(k_topk, dim3(p.T), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1123,7 +1123,7 @@ hipError_t launch_gateup(const GateUpParams &p0, hipStream_t s) {
   const int waves = p.waves_per_expert * p.n;
   const dim3 grid(p.n_shared_blocks + (waves + 3) / 4);
 #define MOE_GU(BITS, XS)                                                                    \
-  MOE_DISPATCH(nch, npass, hipLaunchKernelGGL((k_gateup<BITS, NCH_, NP_, XS>), grid,         \
+  MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_gateup<BITS, NCH_, NP_, XS>), grid,         \
                                               dim3(kBlock), 0, s, p))
   if (p.bits == 4) {
     if (p.xsrc == XS_BF16) { MOE_GU(4, XS_BF16); } else { MOE_GU(4, XS_F32); }
@@ -1153,10 +1153,10 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
 #define MOE_DC(BITS, MAXK, SIN)                                                                   \
   do {                                                                                            \
     if (use_lds)                                                                                  \
-      MOE_DISPATCH(nch, npass, hipLaunchKernelGGL((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, true>), \
+      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, true>), \
                                                   grid, dim3(kBlock), lds, s, p));                \
     else                                                                                          \
-      MOE_DISPATCH(nch, npass, hipLaunchKernelGGL((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, false>), \
+      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, false>), \
                                                   grid, dim3(kBlock), 0, s, p));                  \
   } while (0)
     if (bits == 4) {
@@ -1172,7 +1172,7 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
     const int waves = p.waves_per_expert * p.n;
     const dim3 grid((waves + 3) / 4);
 #define MOE_DY(BITS)                                                                           \
-  MOE_DISPATCH(nch, npass, hipLaunchKernelGGL((k_down_y<BITS, NCH_, NP_>), grid, dim3(kBlock),  \
+  MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_y<BITS, NCH_, NP_>), grid, dim3(kBlock),  \
                                               0, s, p))
     if (bits == 4) { MOE_DY(4); } else { MOE_DY(2); }
 #undef MOE_DY

@@ -6,6 +6,9 @@
 
 namespace moe_impl {
 
+thread_local LaunchEvents g_launch_events;
+
+
 // ---------------------------------------------------------------------------
 // elementwise combine (stand-alone entry point)
 // ---------------------------------------------------------------------------
@@ -115,13 +118,13 @@ __global__ __launch_bounds__(kBlock) void k_copy_f32(float *dst, const float *sr
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_combine(const CombineParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3((p.H + kBlock - 1) / kBlock), dim3(kBlock), 0, s, p);
+  MOE_LAUNCH(k_combine, dim3((p.H + kBlock - 1) / kBlock), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_fill(const FillParams &p, hipStream_t s) {
   const dim3 grid(1024, p.n);
-  hipLaunchKernelGGL(k_fill, grid, dim3(kBlock), 0, s, p);
+  MOE_LAUNCH(k_fill, grid, dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
@@ -130,13 +133,13 @@ hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t s) {
   size_t blocks = (bytes / 16 + kBlock - 1) / kBlock;
   if (blocks < 1) blocks = 1;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(kBlock), 0, s,
+  MOE_LAUNCH(k_zero, dim3((unsigned)blocks), dim3(kBlock), 0, s,
                      static_cast<uint8_t *>(ptr), bytes);
   return hipGetLastError();
 }
 
 hipError_t launch_copy_f32(float *dst, const float *src, int n, hipStream_t s) {
-  hipLaunchKernelGGL(k_copy_f32, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, dst, src, n);
+  MOE_LAUNCH(k_copy_f32, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, dst, src, n);
   return hipGetLastError();
 }
 

@@ -232,10 +232,12 @@ enum {
     MOE_KERNEL_OTHER = 7
 };
 /* Between moe_profile_begin and moe_profile_end, on the calling thread, every
- * kernel launch of the path entry points is bracketed by two HIP events on
- * its stream (not while the stream is being captured into a graph).  Up to
- * max_launches launches are recorded; later ones are not.  The events are
- * created here and destroyed by moe_profile_end. */
+ * kernel launch of the path entry points records two HIP events through its
+ * own dispatch (hipExtLaunchKernel: the events mark the kernel's start and
+ * end, with no marker packets in between), except while its stream is being
+ * captured into a graph.  Up to max_launches launches are recorded; later
+ * ones are not.  The events are created here and destroyed by
+ * moe_profile_end.  Kernel tracers that wrap launches distort these times. */
 int moe_profile_begin(int max_launches);
 /* Wait for the recorded launches and write, in launch order, the elapsed
  * milliseconds between each launch's two events (ms[i]) and its kernel id
