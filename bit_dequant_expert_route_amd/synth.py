@@ -303,6 +303,9 @@ CONFIGS = {
     "q4_stack": LayerConfig("q4_stack", 4096, 1024, 512, 4, 4, 4, "bf16", "bf16", "f32", n_layers=60),
     # 16-token micro-batch on the Qwen-shaped layer
     "q4_batch16": LayerConfig("q4_batch16", 4096, 1024, 512, 4, 4, 4, "bf16", "bf16", "bf16", n_tokens=16),
+    # small parity cases of the stack and batch paths
+    "tiny_stack": LayerConfig("tiny_stack", 256, 128, 16, 2, 4, 4, "bf16", "bf16", "f32", n_layers=8),
+    "tiny_batch": LayerConfig("tiny_batch", 256, 128, 16, 2, 4, 4, "bf16", "bf16", "bf16", n_tokens=7),
 }
 
 ROUTER_STD = 0.02
@@ -341,6 +344,14 @@ def layer_update(cfg: LayerConfig, seed: int, layer: int, attempt: int = 0) -> n
 
 def stack_h0(cfg: LayerConfig, seed: int, token: int = 0) -> np.ndarray:
     return normals((cfg.hidden,), 1.0, seed, STREAM_H0, token).astype(np.float32)
+
+
+def token_residual(cfg: LayerConfig, seed: int, rho: float, token: int, attempt: int = 0) -> np.ndarray:
+    """fp32 residual of one token of a correlated batch: sqrt(rho) z0 +
+    sqrt(1 - rho) z_t, with z_t redrawn per token (attempt) on its own."""
+    z0 = normals((cfg.hidden,), 1.0, seed, STREAM_TOKEN_BASE)
+    zt = normals((cfg.hidden,), 1.0, seed, STREAM_TOKEN, token, attempt)
+    return (np.sqrt(rho) * z0 + np.sqrt(1.0 - rho) * zt).astype(np.float32)
 
 
 def batch_residuals(cfg: LayerConfig, seed: int, rho: float, attempt: int = 0) -> np.ndarray:

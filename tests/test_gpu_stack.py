@@ -1,0 +1,99 @@
+"""GPU parity of the resident expert stack (inter-layer step h += u_l,
+x = RMSNorm(h) in fp32, then the layer) against the oracle walking the same
+layers in fp64.  Per layer the selected experts must match as a set and their
+weights per index; the final residual stream and each layer's weights meet
+err_metric <= 2e-3."""
+import numpy as np
+import pytest
+import torch
+
+from bit_dequant_expert_route_amd import synth
+from cases import TOL, err_metric, make_stack_case
+from gpu_util import log, to_dev, upload_router
+
+pytestmark = pytest.mark.gpu
+
+
+def _build(cfg, case):
+    from bit_dequant_expert_route_amd import moe
+    rb = synth.record_layout(cfg.hidden, cfg.inter, cfg.bits_routed).total
+    sb = synth.record_layout(cfg.hidden, cfg.inter, cfg.bits_shared).total
+    layers, keep = [], []
+    for l in range(case.n_layers):
+        pool = torch.empty(cfg.n_experts * rb, dtype=torch.uint8, device="cuda")
+        moe.fill_experts(pool, rb, cfg.n_experts, case.seed, l, 0, cfg.hidden, cfg.inter,
+                         cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
+        shared = torch.empty(sb, dtype=torch.uint8, device="cuda")
+        moe.fill_experts(shared, sb, 1, case.seed, l, synth.SHARED_GEN_ID, cfg.hidden, cfg.inter,
+                         cfg.bits_shared, synth.dist_for_bits(cfg.bits_shared))
+        layers.append(moe.Layer(hidden=cfg.hidden, inter=cfg.inter, n_experts=cfg.n_experts,
+                                top_k=cfg.top_k, bits_routed=cfg.bits_routed,
+                                bits_shared=cfg.bits_shared, renorm=True,
+                                router=upload_router(case.routers[l], cfg.router_dtype),
+                                gate_vec=upload_router(case.gates[l], cfg.gate_dtype),
+                                experts=pool, expert_stride=rb, shared_expert=shared))
+    stack = moe.Stack(layers)
+    updates = to_dev(case.updates.astype(np.uint16).view(np.int16)).view(torch.bfloat16)
+    return stack, updates
+
+
+def _check(case, h, idx_log, w_log):
+    K = case.cfg.top_k
+    for l in range(case.n_layers):
+        g = [int(e) for e in idx_log[l]]
+        r = [int(e) for e in case.idx[l]]
+        assert sorted(g) == sorted(r), (l, g, r)
+        w_by = np.array([w_log[l][g.index(e)] for e in r])
+        assert err_metric(w_by, case.w[l]) <= TOL, (l, w_by, case.w[l])
+    e = err_metric(h, case.h)
+    assert e <= TOL, e
+    return e
+
+
+def _run(cfg, seed, n_layers=None, graph_replays=0):
+    from bit_dequant_expert_route_amd import moe
+    case = make_stack_case(cfg, seed, n_layers)
+    log(f"stack {cfg.name} seed {seed}: {case.n_layers} layers, update redraws {sum(case.attempts)}")
+    stack, updates = _build(cfg, case)
+    ws = stack.workspace()
+    K, L = cfg.top_k, case.n_layers
+    h = to_dev(case.h0)
+    idx_log = torch.empty(L, K, dtype=torch.int32, device="cuda")
+    w_log = torch.empty(L, K, dtype=torch.float32, device="cuda")
+    moe.stack_decode(stack, updates, h, idx_log, w_log, ws)
+    torch.cuda.synchronize()
+    eager = h.cpu().numpy()
+    err = _check(case, eager, idx_log.cpu().numpy(), w_log.cpu().numpy())
+    log(f"  eager: err(h) {err:.2e}")
+    if graph_replays:
+        s = torch.cuda.Stream()
+        h0 = to_dev(case.h0)
+        with torch.cuda.stream(s):
+            g = moe.graph_stack(stack, updates, h, idx_log, w_log, ws, s)
+        for r in range(graph_replays):
+            h.copy_(h0)
+            idx_log.zero_()
+            torch.cuda.synchronize()
+            g.launch(s)
+            torch.cuda.synchronize()
+            got = h.cpu().numpy()
+            assert np.array_equal(got, eager), f"replay {r} differs from the eager run"
+            _check(case, got, idx_log.cpu().numpy(), w_log.cpu().numpy())
+        g.destroy()
+        log(f"  {graph_replays} graph replays equal the eager run bit for bit")
+    return err
+
+
+@pytest.mark.parametrize("seed", [3, 11])
+def test_tiny_stack(seed):
+    _run(synth.CONFIGS["tiny_stack"], seed, graph_replays=3 if seed == 3 else 0)
+
+
+def test_q4_stack_60_layers():
+    """The 60-layer, 217 GB resident stack at its full size (one token)."""
+    cfg = synth.CONFIGS["q4_stack"]
+    free, total = torch.cuda.mem_get_info()
+    need = cfg.n_layers * (cfg.n_experts * cfg.record_bytes + cfg.shared_record_bytes) + (4 << 30)
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory, {free / 2**30:.0f} GiB free")
+    _run(cfg, 3, graph_replays=1)
