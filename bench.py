@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--instances", type=int, default=128)
-    ap.add_argument("--workload", default="q4_layer", choices=["q4_layer", "q2_layer"])
+    ap.add_argument("--workload", default="q4_layer",
+                    choices=["q4_layer", "q2_layer", "q4_stack", "q4_batch16"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-passes", type=int, default=3)
@@ -157,6 +158,171 @@ def cpu_baseline(cfg, budget_s):
                        f"(fp64 oracle, OpenMP over output rows, weight generation excluded), median")
 
 
+def bench_stack(cfg, args):
+    """One token through the resident 60-layer stack (217 GB at 4 bits): a HIP
+    graph of the whole stack, replayed; every layer has its own 512 experts, so
+    nothing is cache-resident.  Returns (ms per token, per-kernel live us)."""
+    import torch
+    from bit_dequant_expert_route_amd import moe, synth
+    H, I, E, L = cfg.hidden, cfg.inter, cfg.n_experts, cfg.n_layers
+    rb = synth.record_layout(H, I, cfg.bits_routed).total
+    sb = synth.record_layout(H, I, cfg.bits_shared).total
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3000)
+    layers, keep = [], []
+    for l in range(L):
+        pool = torch.empty(E * rb, dtype=torch.uint8, device="cuda")
+        moe.fill_experts(pool, rb, E, 3000, l, 0, H, I, cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
+        shared = torch.empty(sb, dtype=torch.uint8, device="cuda")
+        moe.fill_experts(shared, sb, 1, 3000, l, synth.SHARED_GEN_ID, H, I, cfg.bits_shared,
+                         synth.dist_for_bits(cfg.bits_shared))
+        router = (torch.randn(E, H, generator=g, device="cuda") * synth.ROUTER_STD).to(torch.bfloat16)
+        gate = (torch.randn(H, generator=g, device="cuda") * synth.GATEVEC_STD).to(torch.bfloat16)
+        layers.append(moe.Layer(hidden=H, inter=I, n_experts=E, top_k=cfg.top_k,
+                                bits_routed=cfg.bits_routed, bits_shared=cfg.bits_shared,
+                                renorm=True, router=router, gate_vec=gate, experts=pool,
+                                expert_stride=rb, shared_expert=shared))
+    stack = moe.Stack(layers)
+    ws = stack.workspace()
+    updates = torch.randn(L, H, generator=g, device="cuda").to(torch.bfloat16)
+    h = torch.randn(H, generator=g, device="cuda")
+    K = cfg.top_k
+    idx_log = torch.empty(L, K, dtype=torch.int32, device="cuda")
+    w_log = torch.empty(L, K, device="cuda")
+    moe.stack_decode(stack, updates, h, idx_log, w_log, ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        graph = moe.graph_stack(stack, updates, h, idx_log, w_log, ws, s)
+    for _ in range(args.warmup):
+        graph.launch(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(args.steps):
+        graph.launch(s)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert bool(torch.isfinite(h).all())
+    n_launch = args.profile_passes * L * 4 + 4
+    moe.profile_begin(n_launch)
+    for _ in range(args.profile_passes):
+        moe.stack_decode(stack, updates, h, idx_log, w_log, ws)
+    rec = moe.profile_end(n_launch)
+    graph.destroy()
+    return ms, rec, dict(layers=L, distinct=None)
+
+
+def bench_batch(cfg, args):
+    """Rotation set of R 16-token layer calls over one 512-expert pool; tokens of
+    an instance are correlated (h_t = sqrt(0.5) z0 + sqrt(0.5) z_t) so that each
+    call touches about 40 distinct routed experts."""
+    import torch
+    from bit_dequant_expert_route_amd import moe, synth
+    H, I, E, T, K = cfg.hidden, cfg.inter, cfg.n_experts, cfg.n_tokens, cfg.top_k
+    R = min(args.instances, 16)
+    rb = synth.record_layout(H, I, cfg.bits_routed).total
+    sb = synth.record_layout(H, I, cfg.bits_shared).total
+    pool = torch.empty(E * rb, dtype=torch.uint8, device="cuda")
+    moe.fill_experts(pool, rb, E, 4000, 0, 0, H, I, cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
+    shared = torch.empty(R * sb, dtype=torch.uint8, device="cuda")
+    moe.fill_experts(shared, sb, R, 4000, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared,
+                     synth.dist_for_bits(cfg.bits_shared))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4000)
+    layers, xs, hres = [], [], []
+    for i in range(R):
+        router = (torch.randn(E, H, generator=g, device="cuda") * synth.ROUTER_STD).to(torch.bfloat16)
+        gate = (torch.randn(H, generator=g, device="cuda") * synth.GATEVEC_STD).to(torch.bfloat16)
+        z0 = torch.randn(1, H, generator=g, device="cuda")
+        h = (0.5 ** 0.5) * z0 + (0.5 ** 0.5) * torch.randn(T, H, generator=g, device="cuda")
+        x = (h / torch.sqrt(torch.mean(h * h, dim=1, keepdim=True) + 1e-6)).to(torch.bfloat16)
+        layers.append(moe.Layer(hidden=H, inter=I, n_experts=E, top_k=K,
+                                bits_routed=cfg.bits_routed, bits_shared=cfg.bits_shared,
+                                renorm=True, router=router, gate_vec=gate, experts=pool,
+                                expert_stride=rb, shared_expert=shared[i * sb:(i + 1) * sb]))
+        xs.append(x.contiguous())
+        hres.append(h.contiguous())
+    out = torch.empty(T, H, device="cuda")
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, device="cuda")
+    ws = layers[0].workspace(T)
+    distinct = []
+    for i in range(R):
+        moe.layer_decode(layers[i], xs[i], hres[i], out, idx, w, ws)
+        distinct.append(len(set(idx.cpu().numpy().reshape(-1).tolist())))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        moe.capture_begin(s)
+        for i in range(R):
+            moe.layer_decode(layers[i], xs[i], hres[i], out, idx, w, ws, stream=s)
+        graph = moe.capture_end(s, keep=(layers, xs, hres, out, idx, w, ws))
+    for _ in range(args.warmup):
+        graph.launch(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(args.steps):
+        graph.launch(s)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps / R
+    n_launch = args.profile_passes * R * (4 + 4 * T)
+    moe.profile_begin(n_launch)
+    for _ in range(args.profile_passes):
+        for i in range(R):
+            moe.layer_decode(layers[i], xs[i], hres[i], out, idx, w, ws)
+    rec = moe.profile_end(n_launch)
+    graph.destroy()
+    return ms, rec, dict(instances=R, distinct=float(np.mean(distinct)))
+
+
+def bench_layer(cfg, args):
+    """Rotation set of R single-token layer decodes captured in one graph;
+    returns (ms per layer, per-kernel live records, extras)."""
+    import torch
+    from bit_dequant_expert_route_amd import moe
+    R = args.instances
+    layers, xs, hres, pool, shared = build_rotation(cfg, R)
+    K = cfg.top_k
+    out = torch.empty(cfg.hidden, device="cuda")
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    w = torch.empty(K, device="cuda")
+    ws = layers[0].workspace(1)
+
+    def one_pass(stream=None):
+        for i in range(R):
+            moe.layer_decode(layers[i], xs[i], hres[i], out, idx, w, ws, stream=stream)
+
+    one_pass()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        moe.capture_begin(s)
+        one_pass(s)
+        graph = moe.capture_end(s, keep=(layers, xs, hres, out, idx, w, ws))
+    for _ in range(args.warmup):
+        graph.launch(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(args.steps):
+        graph.launch(s)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms_layer = e0.elapsed_time(e1) / args.steps / R
+    # per-kernel durations (events recorded by each dispatch, eager launches)
+    n_launch = args.profile_passes * R * 4
+    moe.profile_begin(n_launch)
+    for _ in range(args.profile_passes):
+        one_pass()
+    rec = moe.profile_end(n_launch)
+    graph.destroy()
+    return ms_layer, rec, {}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -176,45 +342,31 @@ def main():
         return
 
     cfg = synth.CONFIGS[args.workload]
-    R = args.instances
     kb = kernel_bytes(cfg)
-    layers, xs, hres, pool, shared = build_rotation(cfg, R)
-    K = cfg.top_k
-    out = torch.empty(cfg.hidden, device="cuda")
-    idx = torch.empty(K, dtype=torch.int32, device="cuda")
-    w = torch.empty(K, device="cuda")
-    ws = layers[0].workspace(1)
+    if cfg.n_layers > 1:
+        ms_token, rec, extra = bench_stack(cfg, args)
+        us_per_layer = ms_token * 1000.0 / cfg.n_layers
+        ms_per_step = ms_token
+        unit_note = {"stack_us_per_token": round(ms_token * 1000.0, 2),
+                     "stack_tokens_per_s": round(1000.0 / ms_token, 2)}
+        bytes_per_unit = kb["layer_total"]
+    elif cfg.n_tokens > 1:
+        ms_call, rec, extra = bench_batch(cfg, args)
+        us_per_layer = ms_call * 1000.0
+        ms_per_step = ms_call * extra["instances"]
+        unit_note = {"tokens_per_call": cfg.n_tokens, "distinct_routed_experts": extra["distinct"],
+                     "tokens_per_s": round(cfg.n_tokens * 1e6 / us_per_layer, 1)}
+        # weights of the distinct experts + the shared one + the router, once
+        bytes_per_unit = int(extra["distinct"] * cfg.record_bytes + cfg.shared_record_bytes
+                             + cfg.n_experts * cfg.hidden * 2 + cfg.hidden * 2
+                             + cfg.n_tokens * 40960)
+    else:
+        ms_layer, rec, extra = bench_layer(cfg, args)
+        us_per_layer = ms_layer * 1000.0
+        ms_per_step = ms_layer * args.instances
+        unit_note = {"layer_instances_per_step": args.instances}
+        bytes_per_unit = kb["layer_total"]
 
-    def one_pass(stream=None):
-        for i in range(R):
-            moe.layer_decode(layers[i], xs[i], hres[i], out, idx, w, ws, stream=stream)
-
-    one_pass()
-    torch.cuda.synchronize()
-
-    s = torch.cuda.Stream()
-    with torch.cuda.stream(s):
-        moe.capture_begin(s)
-        one_pass(s)
-        graph = moe.capture_end(s, keep=(layers, xs, hres, out, idx, w, ws))
-    for _ in range(args.warmup):
-        graph.launch(s)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(args.steps):
-        graph.launch(s)
-    e1.record(s)
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    us_per_layer = ms_per_step * 1000.0 / R
-
-    # per-kernel durations (events recorded by each dispatch, eager launches)
-    n_launch = args.profile_passes * R * 4
-    moe.profile_begin(n_launch)
-    for _ in range(args.profile_passes):
-        one_pass()
-    rec = moe.profile_end(n_launch)
     per = {}
     for name, ms in rec:
         per.setdefault(name, []).append(ms)
@@ -222,7 +374,12 @@ def main():
     dom = "gateup"
     achieved = kb[dom] / (kern_us[dom] * 1e-6) / 1e9
     traffic = traffic_from_profiles(args.workload, dom)
-
+    descr = {
+        "q4_layer": "MoE layer decode, batch 1",
+        "q2_layer": "MoE layer decode, batch 1",
+        "q4_stack": f"{cfg.n_layers}-layer resident expert stack, one token (value = per-token time / {cfg.n_layers})",
+        "q4_batch16": f"MoE layer call on {cfg.n_tokens} correlated tokens (value = time per call)",
+    }[cfg.name]
     line = {
         "metric": METRIC,
         "value": round(us_per_layer, 3),
@@ -236,13 +393,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: MoE layer decode, batch 1, hidden {cfg.hidden}, "
+        "config": {"workload": f"{cfg.name}: {descr}, hidden {cfg.hidden}, "
                                f"expert intermediate {cfg.inter}, {cfg.n_experts} experts, "
-                               f"top-{K} + 1 shared, {cfg.bits_routed}-bit experts (group 64, bf16 "
-                               f"scale/bias), bf16 router and x",
-                   "layer_instances_per_step": R, "hbm_bytes_per_layer": kb["layer_total"]},
-        "effective_GBps": round(kb["layer_total"] / (us_per_layer * 1e-6) / 1e9, 1),
-        "pct_hbm_peak": round(100.0 * kb["layer_total"] / (us_per_layer * 1e-6) / 1e9 / PEAK_GBPS, 2),
+                               f"top-{cfg.top_k} + 1 shared, {cfg.bits_routed}-bit experts (group 64, bf16 "
+                               f"scale/bias), bf16 router, {cfg.x_dtype} x",
+                   "hbm_bytes_per_unit": bytes_per_unit, **unit_note},
+        "effective_GBps": round(bytes_per_unit / (us_per_layer * 1e-6) / 1e9, 1),
+        "pct_hbm_peak": round(100.0 * bytes_per_unit / (us_per_layer * 1e-6) / 1e9 / PEAK_GBPS, 2),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
         "roofline": {"bound": "hbm", "kernel": "k_gateup (shared + routed gate/up + SwiGLU)",
                      "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
@@ -250,7 +407,6 @@ def main():
                      "bytes_per_launch": kb[dom]},
         "cpu_baseline": None,
     }
-    del graph
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
