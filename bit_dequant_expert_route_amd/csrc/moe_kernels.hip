@@ -307,6 +307,7 @@ __device__ __forceinline__ XRaw<BITS, XS> load_raw(const void *x, const float *x
   const int col0 = c * ChunkGeom<BITS>::kCols;
   const uint4 *p;
   if constexpr (XS == XS_BF16) p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + col0);
+  else if constexpr (XS == XS_LDSPAD) p = reinterpret_cast<const uint4 *>(xl + c * (ChunkGeom<BITS>::kCols + kLdsPad));
   else p = reinterpret_cast<const uint4 *>(((XS == XS_F32) ? static_cast<const float *>(x) : xl) + col0);
 #pragma unroll
   for (int i = 0; i < XRaw<BITS, XS>::kN; ++i) r.u[i] = p[i];
@@ -572,9 +573,28 @@ __device__ __forceinline__ void topk_store(int e, float w, int K, int32_t *idx, 
 // chunks lane, lane+64, ... of the row.  fp32 accumulation in two chains per
 // lane, then a 6-step tree: reduction depth stays <= 40 for H = 4096, which
 // bounds the fp32 error of a logit well below the top-K gap.
+// the first 512 16-byte chunks of a row (all of a bf16 row up to 4096
+// columns), loaded ahead of the activations they meet
+struct RowPre {
+  uint4 w[8];
+};
+
+__device__ __forceinline__ RowPre row_prefetch(const void *row, int dtype, int H) {
+  RowPre r;
+  const int U = dtype == 1 ? H / 8 : H / 4;
+  const uint4 *W = static_cast<const uint4 *>(row);
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int c = jj * 64 + lane_id();
+    r.w[jj] = W[c < U ? c : 0];
+  }
+  return r;
+}
+
 template <int XS>
 __device__ __forceinline__ float row_dot(const void *row, int dtype, int H, const void *x,
-                                         const float *xl, int t) {
+                                         const float *xl, int t, const RowPre &pre = RowPre{},
+                                         bool use_pre = false) {
   const int lane = lane_id();
   float acc0 = 0.f, acc1 = 0.f;
   if (dtype == 1) {  // bf16 row: chunk c = columns 8c .. 8c+7
@@ -588,7 +608,7 @@ __device__ __forceinline__ float row_dot(const void *row, int dtype, int H, cons
       for (int jj = 0; jj < 8; ++jj) {
         const int c = j0 + jj * 64 + lane;
         const int cc = c < U ? c : 0;
-        wv[jj] = W[cc];
+        wv[jj] = (use_pre && j0 == 0) ? pre.w[jj] : W[cc];
         if constexpr (XS == XS_BF16) {
           xh[jj] = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (size_t)t * H)[cc];
         } else {
@@ -624,7 +644,13 @@ __device__ __forceinline__ float row_dot(const void *row, int dtype, int H, cons
       for (int jj = 0; jj < 8; ++jj) {
         const int c = j0 + jj * 64 + lane;
         const int cc = c < U ? c : 0;
-        wv[jj] = W[cc];
+        if (use_pre && j0 == 0) {
+          const uint4 u = pre.w[jj];
+          wv[jj] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                               __uint_as_float(u.w));
+        } else {
+          wv[jj] = W[cc];
+        }
         if constexpr (XS == XS_BF16) {
           const uint2 u = reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + (size_t)t * H)[cc];
           xv[jj] = make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y));
@@ -647,15 +673,38 @@ __device__ __forceinline__ float row_dot(const void *row, int dtype, int H, cons
 
 // x = (h + u) / sqrt(mean((h + u)^2) + 1e-6) into LDS, two passes
 // ([openclawradar] "Metal compute shaders": RMS normalisation in two passes)
+// x = RMSNorm(h + u) into LDS (every workgroup), h + u and x also to global
+// memory from workgroup 0.  Each thread takes 4 consecutive columns per
+// step; all loads are issued before the first use.
 __device__ __forceinline__ void norm_prologue(const HeadParams &p, float *xl) {
   __shared__ float red[kBlock / 64];
+  constexpr int kSteps = kMaxDim / (4 * kBlock);
   const int H = p.H;
+  float4 hv[kSteps];
+  uint2 uv[kSteps];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int c = (i * kBlock + threadIdx.x) * 4;
+    const int cc = c < H ? c : 0;
+    hv[i] = *reinterpret_cast<const float4 *>(p.h_in + cc);
+    uv[i] = p.upd ? *reinterpret_cast<const uint2 *>(p.upd + cc) : make_uint2(0u, 0u);
+  }
   float ss = 0.f;
-  for (int c = threadIdx.x; c < H; c += kBlock) {
-    float v = p.h_in[c];
-    if (p.upd) v += __uint_as_float(static_cast<uint32_t>(p.upd[c]) << 16);
-    xl[c] = v;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int c = (i * kBlock + threadIdx.x) * 4;
+    if (c < H) {
+      float4 v = hv[i];
+      v.x += bf_lo(uv[i].x);
+      v.y += bf_hi(uv[i].x);
+      v.z += bf_lo(uv[i].y);
+      v.w += bf_hi(uv[i].y);
+      hv[i] = v;
+      ss = fmaf(v.x, v.x, ss);
+      ss = fmaf(v.y, v.y, ss);
+      ss = fmaf(v.z, v.z, ss);
+      ss = fmaf(v.w, v.w, ss);
+    }
   }
   ss = seg_sum(ss, 6);
   if (lane_id() == 0) red[threadIdx.x >> 6] = ss;
@@ -665,13 +714,17 @@ __device__ __forceinline__ void norm_prologue(const HeadParams &p, float *xl) {
   for (int i = 0; i < kBlock / 64; ++i) tot += red[i];
   const float rinv = 1.0f / sqrtf(tot / (float)H + 1e-6f);
   const bool w0 = blockIdx.x == 0;
-  for (int c = threadIdx.x; c < H; c += kBlock) {
-    const float v = xl[c];
-    const float xv = v * rinv;
-    xl[c] = xv;
-    if (w0) {
-      if (p.hres_out) p.hres_out[c] = v;
-      if (p.x_out) p.x_out[c] = xv;
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int c = (i * kBlock + threadIdx.x) * 4;
+    if (c < H) {
+      const float4 v = hv[i];
+      const float4 xv = make_float4(v.x * rinv, v.y * rinv, v.z * rinv, v.w * rinv);
+      *reinterpret_cast<float4 *>(xl + c) = xv;
+      if (w0) {
+        if (p.hres_out) *reinterpret_cast<float4 *>(p.hres_out + c) = v;
+        if (p.x_out) *reinterpret_cast<float4 *>(p.x_out + c) = xv;
+      }
     }
   }
   __syncthreads();
@@ -698,9 +751,23 @@ __device__ __forceinline__ void write_xstage(const void *x, int H, uint32_t *pai
 template <int XS, int BITS_S, int NCH_S, int NPASS_S>
 __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
   extern __shared__ float xl[];
-  if constexpr (XS == XS_NORM) norm_prologue(p, xl);
   const int wv = wave_uniform(threadIdx.x >> 6);
   const int blk = wave_uniform(blockIdx.x);
+  // the stack path normalises x in every workgroup: the router row is
+  // requested first so that its latency overlaps the normalisation
+  RowPre pre{};
+  bool have_pre = false;
+  if constexpr (XS == XS_NORM) {
+    const int unit = blk * (kBlock / 64) + wv;
+    const int row = unit - (unit / (p.E + 1)) * (p.E + 1);
+    if (blk < p.n_router_blocks && unit < p.T * (p.E + 1) && row < p.E) {
+      const size_t esz = p.router_dtype == 1 ? 2 : 4;
+      pre = row_prefetch(static_cast<const uint8_t *>(p.router) + (size_t)row * p.H * esz,
+                         p.router_dtype, p.H);
+      have_pre = true;
+    }
+    norm_prologue(p, xl);
+  }
   if (blk < p.n_router_blocks) {
     const int unit = blk * (kBlock / 64) + wv;  // (token, row) pairs, then the x stager
     const int rows = p.E + 1;
@@ -718,7 +785,7 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
     if (row < p.E) {
       const size_t esz = p.router_dtype == 1 ? 2 : 4;
       const void *wrow = static_cast<const uint8_t *>(p.router) + (size_t)row * p.H * esz;
-      const float d = row_dot<XS>(wrow, p.router_dtype, p.H, p.x, xl, t);
+      const float d = row_dot<XS>(wrow, p.router_dtype, p.H, p.x, xl, t, pre, have_pre);
       if (lane_id() == 0) p.logits[(size_t)t * p.E + row] = d;
     } else {
       const float d = row_dot<XS>(p.gvec, p.gate_dtype, p.H, p.x, xl, t);
@@ -915,8 +982,11 @@ __device__ __forceinline__ void down_accumulate(const float *hin, const RowMap &
 // holds its precomputed down output.
 template <int BITS, int NCH, int NPASS, int MAXK, bool SHARED_IN, bool USE_LDS>
 __global__ __launch_bounds__(kBlock) void k_down_combine(DownParams p) {
-  extern __shared__ float hl[];  // [K (+1)][I]: the SwiGLU outputs, staged once
-  constexpr int XSH = USE_LDS ? XS_NORM : XS_F32;
+  // [K (+1)][I]: the SwiGLU outputs, staged once, each code chunk's columns
+  // followed by kLdsPad unused floats
+  extern __shared__ float hl[];
+  constexpr int XSH = USE_LDS ? XS_LDSPAD : XS_F32;
+  constexpr int NC = ChunkGeom<BITS>::kCols;
   const int wave = wave_uniform(blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6));
   const RowMap m = row_map<BITS>(p.I);
   const int row0 = wave * p.rows_per_wave;
@@ -941,19 +1011,23 @@ __global__ __launch_bounds__(kBlock) void k_down_combine(DownParams p) {
   }
   DnTile<BITS, NCH, NPASS> ts;
   if constexpr (SHARED_IN) down_load(ts, p.shared_rec, p.soff, p.H, m, row0);
+  const int lds_stride = (p.I / NC) * (NC + kLdsPad);  // floats per expert in LDS
   if constexpr (USE_LDS) {
     const int nh = (p.K + (SHARED_IN ? 1 : 0)) * p.I;
     const int nr = p.K * p.I;
     for (int e = threadIdx.x * 4; e < nh; e += kBlock * 4) {
       const float4 v = e < nr ? *reinterpret_cast<const float4 *>(p.h_routed + e)
                               : *reinterpret_cast<const float4 *>(p.h_shared + (e - nr));
-      *reinterpret_cast<float4 *>(hl + e) = v;
+      const int k = e / p.I, col = e - k * p.I;
+      const int chunk = col / NC;
+      *reinterpret_cast<float4 *>(hl + k * lds_stride + chunk * (NC + kLdsPad) + (col - chunk * NC)) = v;
     }
     __syncthreads();
   }
   if (!active) return;
+  const int hstride = USE_LDS ? lds_stride : p.I;
   const float *hr = USE_LDS ? hl : p.h_routed;
-  const float *hs = USE_LDS ? hl + (size_t)p.K * p.I : p.h_shared;
+  const float *hs = USE_LDS ? hl + (size_t)p.K * lds_stride : p.h_shared;
 
   float acc[NPASS];
 #pragma unroll
@@ -962,7 +1036,7 @@ __global__ __launch_bounds__(kBlock) void k_down_combine(DownParams p) {
   for (int k = 0; k < MAXK; ++k) {
     if (k < p.K) {
       const bool v = ids[k] >= 0 && ids[k] < p.E;
-      down_accumulate<BITS, NCH, NPASS, XSH>(hr + (size_t)k * p.I, m, p.H, row0, v, wk[k], t[k], acc);
+      down_accumulate<BITS, NCH, NPASS, XSH>(hr + (size_t)k * hstride, m, p.H, row0, v, wk[k], t[k], acc);
     }
   }
   const float sig = p.sigma[0];
@@ -1052,20 +1126,21 @@ static int pick_pass(int tuned, int dflt) {
   return (tuned == 1 || tuned == 2 || tuned == 4) ? tuned : dflt;
 }
 
-// instantiated (NCH, NPASS) pairs; NCH 4 (rows wider than 2048 codes per
-// 64 lanes) only with one pass
+// instantiated (NCH, NPASS) pairs: NCH 2 with at most two passes, NCH 4
+// (rows wider than 2048 codes per 64 lanes) with one
 #define MOE_DISPATCH(nch, npass, ...)                                                    \
   do {                                                                                   \
     if (nch == 1 && npass == 1) { constexpr int NCH_ = 1, NP_ = 1; __VA_ARGS__; }        \
     else if (nch == 1 && npass == 2) { constexpr int NCH_ = 1, NP_ = 2; __VA_ARGS__; }   \
     else if (nch == 1) { constexpr int NCH_ = 1, NP_ = 4; __VA_ARGS__; }                 \
     else if (nch == 2 && npass == 1) { constexpr int NCH_ = 2, NP_ = 1; __VA_ARGS__; }   \
-    else if (nch == 2 && npass == 2) { constexpr int NCH_ = 2, NP_ = 2; __VA_ARGS__; }   \
-    else if (nch == 2) { constexpr int NCH_ = 2, NP_ = 4; __VA_ARGS__; }                 \
+    else if (nch == 2) { constexpr int NCH_ = 2, NP_ = 2; __VA_ARGS__; }                 \
     else { constexpr int NCH_ = 4, NP_ = 1; __VA_ARGS__; }                              \
   } while (0)
 
-static int clamp_pass(int nch, int npass) { return nch >= 4 ? 1 : npass; }
+static int clamp_pass(int nch, int npass) {
+  return nch >= 4 ? 1 : (nch >= 2 && npass > 2 ? 2 : npass);
+}
 
 size_t xstage_pair_bytes(int cols, int bits) {
   return (size_t)(cols * bits / 128) * (64 / bits) * 4;
@@ -1116,7 +1191,7 @@ hipError_t launch_gateup(const GateUpParams &p0, hipStream_t s) {
   GateUpParams p = p0;
   const int nch = nch_for(p.H, p.bits);
   const int rpp = rpp_for(p.H, p.bits);
-  const int npass = clamp_pass(nch, pick_pass(tune().gu, rpp >= 4 ? 1 : 2));
+  const int npass = clamp_pass(nch, pick_pass(tune().gu, rpp >= 2 ? 1 : 2));
   p.rows_per_wave = npass * rpp;
   p.waves_per_expert = (p.I + p.rows_per_wave - 1) / p.rows_per_wave;
   p.n_shared_blocks = p.with_shared ? (p.waves_per_expert + 3) / 4 : 0;
@@ -1139,15 +1214,17 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
   const int bits = p.bits_r;
   const int nch = nch_for(p.I, bits);
   const int rpp = rpp_for(p.I, bits);
-  const int npass = clamp_pass(nch, pick_pass(tune().dn, rpp >= 8 ? 1 : 2));
+  const int npass = clamp_pass(nch, pick_pass(tune().dn, rpp >= 4 ? 1 : (rpp >= 2 ? 2 : 4)));
   p.rows_per_wave = npass * rpp;
   if (p.combine) {
     const bool shared_in = p.h_shared != nullptr;
     const int waves = (p.H + p.rows_per_wave - 1) / p.rows_per_wave;
     const dim3 grid((waves + 3) / 4);
     const bool k4 = p.K <= 4;
-    // the SwiGLU outputs go through LDS when they fit in 64 KiB
-    const size_t hbytes = (size_t)(p.K + (shared_in ? 1 : 0)) * p.I * sizeof(float);
+    // the SwiGLU outputs go through LDS (padded per code chunk) when they fit
+    // in 64 KiB
+    const int nc = 128 / bits;
+    const size_t hbytes = (size_t)(p.K + (shared_in ? 1 : 0)) * (p.I / nc) * (nc + kLdsPad) * sizeof(float);
     const bool use_lds = hbytes <= 65536;
     const size_t lds = use_lds ? hbytes : 0;
 #define MOE_DC(BITS, MAXK, SIN)                                                                   \
