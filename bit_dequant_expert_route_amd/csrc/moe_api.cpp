@@ -80,7 +80,8 @@ bool dim_ok(int d) { return d >= 64 && d <= kMaxDim && d % kGroup == 0; }
 // ---------------------------------------------------------------------------
 struct WsLayout {
   size_t logits, sigma, h_routed, h_shared, y_shared, x_stage, hres_stage, xs_pairs, xs_sums,
-      h_pong, total;
+      h_pong, y_routed, g_count, g_expert, g_start, g_pair, total;
+  size_t xs_pair_stride, xs_sum_stride;  // per token, in u32 / floats
 };
 
 WsLayout ws_layout(const moe_layer_t *L, int T, int n_layers) {
@@ -95,9 +96,20 @@ WsLayout ws_layout(const moe_layer_t *L, int T, int n_layers) {
   w.y_shared = o; o += up256(4 * (size_t)T * H);
   w.x_stage = o; o += up256(4 * H);
   w.hres_stage = o; o += up256(4 * H);
-  w.xs_pairs = o; o += up256(xstage_pair_bytes(L->hidden, L->bits_routed));
-  w.xs_sums = o; o += up256(xstage_sum_bytes(L->hidden, L->bits_routed));
+  // staged bf16 x, one block per token
+  w.xs_pair_stride = up256(xstage_pair_bytes(L->hidden, L->bits_routed)) / 4;
+  w.xs_sum_stride = up256(xstage_sum_bytes(L->hidden, L->bits_routed)) / 4;
+  w.xs_pairs = o; o += 4 * w.xs_pair_stride * (size_t)T;
+  w.xs_sums = o; o += 4 * w.xs_sum_stride * (size_t)T;
   w.h_pong = o; o += n_layers > 0 ? up256(4 * H) : 0;
+  // token batches: per-pair down outputs and the expert groups
+  const size_t P = (size_t)T * K;
+  const bool batch = T > 1;
+  w.y_routed = o; o += batch ? up256(4 * P * H) : 0;
+  w.g_count = o; o += batch ? 256 : 0;
+  w.g_expert = o; o += batch ? up256(4 * (P + 1)) : 0;
+  w.g_start = o; o += batch ? up256(4 * (P + 2)) : 0;
+  w.g_pair = o; o += batch ? up256(4 * P) : 0;
   w.total = o;
   return w;
 }
@@ -217,6 +229,8 @@ int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in
   hp.bits_routed = L->bits_routed;
   hp.xs_pairs = xs_pairs;
   hp.xs_sums = xs_sums;
+  hp.xs_pair_stride = (int)wl.xs_pair_stride;
+  hp.xs_sum_stride = (int)wl.xs_sum_stride;
   MOE_TRY_HIP(timed(s, MOE_KERNEL_HEAD, [&] { return launch_head(hp, s); }), "router/shared launch");
 
   // K2
@@ -499,6 +513,108 @@ int moe_combine(int hidden, int n_routed, const float *h_res, const float *y, co
   return MOE_OK;
 }
 
+// T > 1 tokens through one layer: router rows for every token, then the
+// top-K of every token and the (token, expert) pairs grouped by expert, so
+// that gate/up and down read each distinct expert's weights once for all of
+// its tokens; then the per-token combine
+int layer_batch(const moe_layer_t *L, int T, int xsrc, const void *x, const float *h_res,
+                float *h_out, int32_t *idx, float *w, uint8_t *ws, const WsLayout &wl,
+                hipStream_t s) {
+  float *logits = reinterpret_cast<float *>(ws + wl.logits);
+  float *sigma = reinterpret_cast<float *>(ws + wl.sigma);
+  uint32_t *xs_pairs = xsrc == XS_BF16 ? reinterpret_cast<uint32_t *>(ws + wl.xs_pairs) : nullptr;
+  float *xs_sums = xsrc == XS_BF16 ? reinterpret_cast<float *>(ws + wl.xs_sums) : nullptr;
+  int32_t *g_count = reinterpret_cast<int32_t *>(ws + wl.g_count);
+  int32_t *g_expert = reinterpret_cast<int32_t *>(ws + wl.g_expert);
+  int32_t *g_start = reinterpret_cast<int32_t *>(ws + wl.g_start);
+  int32_t *g_pair = reinterpret_cast<int32_t *>(ws + wl.g_pair);
+
+  HeadParams hp = head_params(L, T);
+  hp.xsrc = xsrc;
+  hp.x = x;
+  hp.logits = logits;
+  hp.sigma = sigma;
+  hp.n_shared_waves = 0;
+  hp.bits_routed = L->bits_routed;
+  hp.xs_pairs = xs_pairs;
+  hp.xs_sums = xs_sums;
+  hp.xs_pair_stride = (int)wl.xs_pair_stride;
+  hp.xs_sum_stride = (int)wl.xs_sum_stride;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_HEAD, [&] { return launch_head(hp, s); }), "router launch");
+
+  RouteGroupParams rg;
+  rg.logits = logits;
+  rg.T = T;
+  rg.E = L->n_experts;
+  rg.K = L->top_k;
+  rg.renorm = L->renorm_topk;
+  rg.idx = idx;
+  rg.w = w;
+  rg.g_count = g_count;
+  rg.g_expert = g_expert;
+  rg.g_start = g_start;
+  rg.g_pair = g_pair;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_TOPK, [&] { return launch_route_group(rg, s); }), "top-K/group launch");
+
+  GroupedParams gp;
+  memset(&gp, 0, sizeof gp);
+  gp.H = L->hidden;
+  gp.I = L->inter;
+  gp.E = L->n_experts;
+  gp.K = L->top_k;
+  gp.T = T;
+  gp.experts = static_cast<const uint8_t *>(L->experts);
+  gp.stride = L->expert_stride;
+  gp.shared_rec = static_cast<const uint8_t *>(L->shared_expert);
+  gp.off = offsets_of(L->hidden, L->inter, L->bits_routed);
+  gp.soff = offsets_of(L->hidden, L->inter, L->bits_shared);
+  gp.g_count = g_count;
+  gp.g_expert = g_expert;
+  gp.g_start = g_start;
+  gp.g_pair = g_pair;
+  gp.xsrc = xsrc;
+  gp.x = x;
+  gp.xs_pairs = xs_pairs;
+  gp.xs_sums = xs_sums;
+  gp.xs_pair_stride = (int)wl.xs_pair_stride;
+  gp.xs_sum_stride = (int)wl.xs_sum_stride;
+  gp.h_routed = reinterpret_cast<float *>(ws + wl.h_routed);
+  gp.h_shared = reinterpret_cast<float *>(ws + wl.h_shared);
+  gp.y_routed = reinterpret_cast<float *>(ws + wl.y_routed);
+  gp.y_shared = reinterpret_cast<float *>(ws + wl.y_shared);
+  const bool same = L->bits_shared == L->bits_routed;
+  // routed groups (and the shared one when it has the same width)
+  GroupedParams gr = gp;
+  gr.bits = L->bits_routed;
+  gr.do_routed = 1;
+  gr.do_shared = same;
+  GroupedParams gs = gp;  // the shared expert alone, at its own width
+  gs.bits = L->bits_shared;
+  gs.do_routed = 0;
+  gs.do_shared = 1;
+  gs.xs_pairs = nullptr;  // x was staged for the routed width
+  gs.xs_sums = nullptr;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_GATEUP, [&] { return launch_gateup_grouped(gr, s); }), "grouped gate/up launch");
+  if (!same)
+    MOE_TRY_HIP(timed(s, MOE_KERNEL_GATEUP, [&] { return launch_gateup_grouped(gs, s); }), "shared gate/up launch");
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_DOWN_Y, [&] { return launch_down_grouped(gr, s); }), "grouped down launch");
+  if (!same)
+    MOE_TRY_HIP(timed(s, MOE_KERNEL_DOWN_Y, [&] { return launch_down_grouped(gs, s); }), "shared down launch");
+
+  CombineTokensParams cp;
+  cp.H = L->hidden;
+  cp.K = L->top_k;
+  cp.T = T;
+  cp.h_res = h_res;
+  cp.y_routed = gp.y_routed;
+  cp.w = w;
+  cp.y_shared = gp.y_shared;
+  cp.sigma = sigma;
+  cp.out = h_out;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_COMBINE, [&] { return launch_combine_tokens(cp, s); }), "combine launch");
+  return MOE_OK;
+}
+
 int moe_layer_decode(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void *x,
                      const float *h_res, float *h_out, int32_t *topk_idx, float *topk_w,
                      void *ws, size_t ws_bytes, void *stream) {
@@ -517,14 +633,12 @@ int moe_layer_decode(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int xsrc = x_dtype == MOE_BF16 ? XS_BF16 : XS_F32;
   const size_t xes = x_dtype == MOE_BF16 ? 2 : 4;
-  const size_t H = L->hidden, K = L->top_k;
-  for (int t = 0; t < n_tokens; ++t) {
-    st = layer_token(L, xsrc, static_cast<const uint8_t *>(x) + t * H * xes, nullptr, nullptr,
-                     h_res + t * H, h_out + t * H, topk_idx + t * K, topk_w + t * K,
+  (void)xes;
+  if (n_tokens > 1)
+    return layer_batch(L, n_tokens, xsrc, x, h_res, h_out, topk_idx, topk_w,
+                       static_cast<uint8_t *>(ws), wl, s);
+  return layer_token(L, xsrc, x, nullptr, nullptr, h_res, h_out, topk_idx, topk_w,
                      static_cast<uint8_t *>(ws), wl, s);
-    if (st != MOE_OK) return st;
-  }
-  return MOE_OK;
 }
 
 int moe_layer_ws_view(const moe_layer_t *L, int n_tokens, void *ws, size_t ws_bytes,

@@ -64,8 +64,62 @@ struct HeadParams {
   int bits_routed;
   uint32_t *xs_pairs;
   float *xs_sums;
+  int xs_pair_stride, xs_sum_stride;  // per token (u32 / floats); one stager unit per token
 };
 hipError_t launch_head(const HeadParams &p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// token batches: top-K of every token, then the (token, expert) pairs sorted
+// by expert (token order kept inside an expert) into groups
+// ---------------------------------------------------------------------------
+struct RouteGroupParams {
+  const float *logits;            // [T][E]
+  int T, E, K, renorm;
+  int32_t *idx;                   // [T][K]
+  float *w;                       // [T][K]
+  int32_t *g_count;               // [1]  number of distinct experts U
+  int32_t *g_expert;              // [U]  ascending expert id
+  int32_t *g_start;               // [U + 1] first position of each group in g_pair
+  int32_t *g_pair;                // [T K] pair index t K + k, grouped
+};
+hipError_t launch_route_group(const RouteGroupParams &p, hipStream_t s);
+
+// gate/up and down over the groups: each wave keeps one expert's weight rows
+// in registers and applies them to every token of the group; the shared
+// expert is one more group holding every token
+struct GroupedParams {
+  int H, I, E, K, T;
+  int bits;                       // width of the experts this launch covers
+  const uint8_t *experts;
+  size_t stride;
+  const uint8_t *shared_rec;
+  RecOffsets off, soff;
+  const int32_t *g_count, *g_expert, *g_start, *g_pair;
+  int do_routed, do_shared;
+  // gate/up input
+  int xsrc;                       // XS_BF16 or XS_F32
+  const void *x;                  // [T][H]
+  const uint32_t *xs_pairs;       // staged bf16 x per token, or null
+  const float *xs_sums;
+  int xs_pair_stride, xs_sum_stride;
+  // SwiGLU outputs (gate/up writes them, down reads them)
+  float *h_routed;                // [T K][I] by pair
+  float *h_shared;                // [T][I]
+  // down outputs
+  float *y_routed;                // [T K][H] by pair
+  float *y_shared;                // [T][H]
+  int rows_per_wave, tiles;       // set by the launcher
+};
+hipError_t launch_gateup_grouped(const GroupedParams &p, hipStream_t s);
+hipError_t launch_down_grouped(const GroupedParams &p, hipStream_t s);
+
+// out[t] = h_res[t] + sum_k w[t][k] y_routed[t K + k] + sigma[t] y_shared[t]
+struct CombineTokensParams {
+  int H, K, T;
+  const float *h_res, *y_routed, *w, *y_shared, *sigma;
+  float *out;
+};
+hipError_t launch_combine_tokens(const CombineTokensParams &p, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // top-K + softmax weights from logits (stand-alone routing entry point)

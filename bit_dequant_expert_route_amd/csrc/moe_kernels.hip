@@ -769,13 +769,17 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
     norm_prologue(p, xl);
   }
   if (blk < p.n_router_blocks) {
-    const int unit = blk * (kBlock / 64) + wv;  // (token, row) pairs, then the x stager
+    const int unit = blk * (kBlock / 64) + wv;  // (token, row) pairs, then one x stager per token
     const int rows = p.E + 1;
-    if (unit == p.T * rows) {
+    if (unit >= p.T * rows) {
+      const int st = unit - p.T * rows;
       if constexpr (XS == XS_BF16) {
-        if (p.xs_pairs) {
-          if (p.bits_routed == 4) write_xstage<4>(p.x, p.H, p.xs_pairs, p.xs_sums);
-          else write_xstage<2>(p.x, p.H, p.xs_pairs, p.xs_sums);
+        if (p.xs_pairs && st < p.T) {
+          const void *xt = static_cast<const uint16_t *>(p.x) + (size_t)st * p.H;
+          uint32_t *pairs = p.xs_pairs + (size_t)st * p.xs_pair_stride;
+          float *sums = p.xs_sums + (size_t)st * p.xs_sum_stride;
+          if (p.bits_routed == 4) write_xstage<4>(xt, p.H, pairs, sums);
+          else write_xstage<2>(xt, p.H, pairs, sums);
         }
       }
       return;
@@ -1085,6 +1089,185 @@ __global__ __launch_bounds__(kBlock) void k_down_y(DownParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// token batches
+// ---------------------------------------------------------------------------
+// One workgroup: the top-K of every token (wave w takes tokens w, w + 4, ...),
+// then a counting sort of the T*K (token, expert) pairs by expert id with the
+// pair order kept inside an expert.  P = T*K <= 512 and the ranks are plain
+// counts over the pairs, so the result does not depend on thread timing.
+__global__ __launch_bounds__(kBlock) void k_route_group(RouteGroupParams p) {
+  __shared__ int pe[kMaxTokens * kMaxK];
+  __shared__ int pless[kMaxTokens * kMaxK];
+  __shared__ unsigned char pfirst[kMaxTokens * kMaxK];
+  __shared__ int n_first;
+  const int wv = threadIdx.x >> 6, lane = lane_id();
+  if (threadIdx.x == 0) n_first = 0;
+  for (int t = wv; t < p.T; t += kBlock / 64) {
+    float v[kTopkNpl];
+    topk_load(p.logits + (size_t)t * p.E, p.E, v);
+    int e;
+    float w;
+    topk_select(v, p.E, p.K, p.renorm, e, w);
+    topk_store(e, w, p.K, p.idx + (size_t)t * p.K, p.w + (size_t)t * p.K);
+    if (lane < p.K) pe[t * p.K + lane] = e;
+  }
+  __syncthreads();
+  const int P = p.T * p.K;
+  int mine = 0;
+  for (int q = threadIdx.x; q < P; q += kBlock) {
+    const int e = pe[q];
+    int less = 0, before = 0;
+    for (int r = 0; r < P; ++r) {
+      const int f = pe[r];
+      less += f < e;
+      before += (r < q) & (f == e);
+    }
+    p.g_pair[less + before] = q;
+    pless[q] = less;
+    pfirst[q] = before == 0;
+    mine += before == 0;
+  }
+  atomicAdd(&n_first, mine);
+  __syncthreads();
+  for (int q = threadIdx.x; q < P; q += kBlock) {
+    if (!pfirst[q]) continue;
+    const int e = pe[q];
+    int g = 0;
+    for (int r = 0; r < P; ++r) g += pfirst[r] & (pe[r] < e);
+    p.g_expert[g] = e;
+    p.g_start[g] = pless[q];
+  }
+  if (threadIdx.x == 0) {
+    p.g_count[0] = n_first;
+    p.g_start[n_first] = P;
+  }
+}
+
+// the group of a work item: its expert (or the shared one) and its tokens;
+// lane j < n holds the j-th (pair, token) of the group
+struct GroupRef {
+  int id, n, pair, tok;
+  bool shared;
+};
+
+__device__ __forceinline__ GroupRef group_ref(const GroupedParams &p, int g, int U) {
+  GroupRef r;
+  const int lane = lane_id();
+  r.shared = p.do_shared && g == U;
+  if (r.shared) {
+    r.id = kSharedId;
+    r.n = p.T;
+    r.pair = lane;
+    r.tok = lane;
+  } else {
+    r.id = wave_uniform(p.g_expert[g]);
+    const int s0 = wave_uniform(p.g_start[g]);
+    r.n = wave_uniform(p.g_start[g + 1]) - s0;
+    r.pair = lane < r.n ? p.g_pair[s0 + lane] : 0;
+    r.tok = r.pair / p.K;
+  }
+  return r;
+}
+
+template <int BITS, int NCH, int XS>
+__device__ __forceinline__ void group_stage(const GroupedParams &p, const RowMap &m, int tok,
+                                            XStage<BITS, XS != XS_BF16> (&xs)[NCH]) {
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c0 = m.li + (j << m.lg);
+    const int c = c0 < m.cpr ? c0 : 0;
+    if constexpr (XS == XS_BF16) {
+      if (p.xs_pairs) {
+        xs[j] = read_stage<BITS>(p.xs_pairs + (size_t)tok * p.xs_pair_stride,
+                                 p.xs_sums + (size_t)tok * p.xs_sum_stride, c);
+        continue;
+      }
+    }
+    const void *xt = XS == XS_BF16
+                         ? static_cast<const void *>(static_cast<const uint16_t *>(p.x) + (size_t)tok * p.H)
+                         : static_cast<const void *>(static_cast<const float *>(p.x) + (size_t)tok * p.H);
+    xs[j] = make_stage<BITS, XS>(xt, nullptr, c);
+  }
+}
+
+template <int BITS, int NCH, int NPASS, int XS>
+__global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedParams p) {
+  constexpr bool XF32 = XS != XS_BF16;
+  const int wave = wave_uniform(blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6));
+  const int nw = gridDim.x * (kBlock / 64);
+  const int U = p.do_routed ? wave_uniform(p.g_count[0]) : 0;
+  const int n_items = (U + (p.do_shared ? 1 : 0)) * p.tiles;
+  const RowMap m = row_map<BITS>(p.H);
+  for (int item = wave; item < n_items; item += nw) {
+    const int g = item / p.tiles;
+    const int row0 = (item - g * p.tiles) * p.rows_per_wave;
+    const GroupRef gr = group_ref(p, g, U);
+    const bool valid = gr.shared ? true : (gr.id >= 0 && gr.id < p.E);
+    const uint8_t *rec = gr.shared ? p.shared_rec : p.experts + (size_t)(valid ? gr.id : 0) * p.stride;
+    GUTile<BITS, NCH, NPASS> tile;
+    gu_load(tile, rec, gr.shared ? p.soff : p.off, m, p.I, row0);
+    // tokens of the group, the next token's x staged while this one computes
+    XStage<BITS, XF32> cur[NCH];
+    group_stage<BITS, NCH, XS>(p, m, __builtin_amdgcn_readlane(gr.tok, 0), cur);
+    for (int i = 0; i < gr.n; ++i) {
+      const int pair = __builtin_amdgcn_readlane(gr.pair, i);
+      const int tok = __builtin_amdgcn_readlane(gr.tok, i);
+      XStage<BITS, XF32> nxt[NCH];
+      if (i + 1 < gr.n) group_stage<BITS, NCH, XS>(p, m, __builtin_amdgcn_readlane(gr.tok, i + 1), nxt);
+      float *hout = gr.shared ? p.h_shared + (size_t)tok * p.I : p.h_routed + (size_t)pair * p.I;
+      gu_compute(tile, cur, m, p.I, row0, valid, hout);
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) cur[j] = nxt[j];
+    }
+  }
+}
+
+template <int BITS, int NCH, int NPASS>
+__global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedParams p) {
+  const int wave = wave_uniform(blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6));
+  const int nw = gridDim.x * (kBlock / 64);
+  const int U = p.do_routed ? wave_uniform(p.g_count[0]) : 0;
+  const int n_items = (U + (p.do_shared ? 1 : 0)) * p.tiles;
+  const RowMap m = row_map<BITS>(p.I);
+  for (int item = wave; item < n_items; item += nw) {
+    const int g = item / p.tiles;
+    const int row0 = (item - g * p.tiles) * p.rows_per_wave;
+    const GroupRef gr = group_ref(p, g, U);
+    const bool valid = gr.shared ? true : (gr.id >= 0 && gr.id < p.E);
+    const uint8_t *rec = gr.shared ? p.shared_rec : p.experts + (size_t)(valid ? gr.id : 0) * p.stride;
+    DnTile<BITS, NCH, NPASS> tile;
+    down_load(tile, rec, gr.shared ? p.soff : p.off, p.H, m, row0);
+    for (int i = 0; i < gr.n; ++i) {
+      const int pair = __builtin_amdgcn_readlane(gr.pair, i);
+      const int tok = __builtin_amdgcn_readlane(gr.tok, i);
+      const float *hin = gr.shared ? p.h_shared + (size_t)tok * p.I : p.h_routed + (size_t)pair * p.I;
+      float *yout = gr.shared ? p.y_shared + (size_t)tok * p.H : p.y_routed + (size_t)pair * p.H;
+      float acc[NPASS];
+#pragma unroll
+      for (int k = 0; k < NPASS; ++k) acc[k] = 0.f;
+      down_accumulate<BITS, NCH, NPASS, XS_F32>(hin, m, p.H, row0, valid, 1.0f, tile, acc);
+#pragma unroll
+      for (int k = 0; k < NPASS; ++k) {
+        const float sum = seg_sum(acc[k], m.lg);
+        const int r = row0 + k * m.rpp + m.rip;
+        if (m.li == 0 && r < p.H) yout[r] = sum;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_combine_tokens(CombineTokensParams p) {
+  const int o = blockIdx.x * kBlock + threadIdx.x;
+  const int t = blockIdx.y;
+  if (o >= p.H) return;
+  float acc = p.h_res[(size_t)t * p.H + o];
+  for (int k = 0; k < p.K; ++k)
+    acc = fmaf(p.w[t * p.K + k], p.y_routed[(size_t)(t * p.K + k) * p.H + o], acc);
+  acc = fmaf(p.sigma[t], p.y_shared[(size_t)t * p.H + o], acc);
+  p.out[(size_t)t * p.H + o] = acc;
+}
+
+// ---------------------------------------------------------------------------
 // launch shapes
 // ---------------------------------------------------------------------------
 static int nch_for(int cols, int bits) {
@@ -1156,7 +1339,7 @@ hipError_t launch_head(const HeadParams &p0, hipStream_t s) {
     p.shared_rows_per_wave = npass * rpp_for(p.H, bs);
     p.n_shared_waves = (p.I + p.shared_rows_per_wave - 1) / p.shared_rows_per_wave;
   }
-  const int units = p.T * (p.E + 1) + 1;  // rows of every token, then the x stager
+  const int units = p.T * (p.E + 1) + p.T;  // rows of every token, then one x stager per token
   p.n_router_blocks = (units + 3) / 4;
   const int nsb = bs ? (p.n_shared_waves + 3) / 4 : 0;
   const dim3 grid(p.n_router_blocks + nsb);
@@ -1254,6 +1437,62 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
     if (bits == 4) { MOE_DY(4); } else { MOE_DY(2); }
 #undef MOE_DY
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_group(const RouteGroupParams &p, hipStream_t s) {
+  MOE_LAUNCH(k_route_group, dim3(1), dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
+// work items = groups x row tiles, taken by a grid of at most 2048
+// workgroups in a strided loop
+static dim3 grouped_grid(const GroupedParams &p) {
+  const int max_groups = (p.T * p.K < p.E ? p.T * p.K : p.E) + 1;
+  const long items = (long)max_groups * p.tiles;
+  long blocks = (items + 3) / 4;
+  if (blocks > 2048) blocks = 2048;
+  return dim3((unsigned)(blocks < 1 ? 1 : blocks));
+}
+
+hipError_t launch_gateup_grouped(const GroupedParams &p0, hipStream_t s) {
+  GroupedParams p = p0;
+  const int nch = nch_for(p.H, p.bits);
+  const int rpp = rpp_for(p.H, p.bits);
+  const int npass = clamp_pass(nch, pick_pass(tune().gu, rpp >= 2 ? 1 : 2));
+  p.rows_per_wave = npass * rpp;
+  p.tiles = (p.I + p.rows_per_wave - 1) / p.rows_per_wave;
+  const dim3 grid = grouped_grid(p);
+#define MOE_GG(BITS, XS)                                                                    \
+  MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_gateup_grouped<BITS, NCH_, NP_, XS>), grid,       \
+                                      dim3(kBlock), 0, s, p))
+  if (p.bits == 4) {
+    if (p.xsrc == XS_BF16) { MOE_GG(4, XS_BF16); } else { MOE_GG(4, XS_F32); }
+  } else {
+    if (p.xsrc == XS_BF16) { MOE_GG(2, XS_BF16); } else { MOE_GG(2, XS_F32); }
+  }
+#undef MOE_GG
+  return hipGetLastError();
+}
+
+hipError_t launch_down_grouped(const GroupedParams &p0, hipStream_t s) {
+  GroupedParams p = p0;
+  const int nch = nch_for(p.I, p.bits);
+  const int rpp = rpp_for(p.I, p.bits);
+  const int npass = clamp_pass(nch, pick_pass(tune().dn, rpp >= 4 ? 1 : (rpp >= 2 ? 2 : 4)));
+  p.rows_per_wave = npass * rpp;
+  p.tiles = (p.H + p.rows_per_wave - 1) / p.rows_per_wave;
+  const dim3 grid = grouped_grid(p);
+  if (p.bits == 4) {
+    MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_grouped<4, NCH_, NP_>), grid, dim3(kBlock), 0, s, p));
+  } else {
+    MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_grouped<2, NCH_, NP_>), grid, dim3(kBlock), 0, s, p));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_tokens(const CombineTokensParams &p, hipStream_t s) {
+  MOE_LAUNCH(k_combine_tokens, dim3((p.H + kBlock - 1) / kBlock, p.T), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
