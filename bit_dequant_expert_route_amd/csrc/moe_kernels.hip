@@ -996,33 +996,65 @@ __global__ __launch_bounds__(kBlock) void k_down_combine(DownParams p) {
   const int row0 = wave * p.rows_per_wave;
   const bool active = row0 < p.H;
 
+  // Loads in the order their data are needed (vmcnt counts in order): the
+  // selection, the shared expert's rows (known before the selection), the
+  // SwiGLU outputs for LDS, then the routed rows once the ids have arrived.
+  // Only the LDS fill waits at the barrier; each expert's rows are consumed
+  // as they arrive.
   int ids[MAXK];
   float wk[MAXK];
 #pragma unroll
   for (int k = 0; k < MAXK; ++k) {
-    ids[k] = k < p.K ? wave_uniform(p.idx[k]) : -2;
+    ids[k] = k < p.K ? p.idx[k] : -2;
     wk[k] = k < p.K ? p.w[k] : 0.f;
-  }
-  // weight loads first, then h_routed [K][I] and h_shared [I] into LDS in
-  // one coalesced pass
-  DnTile<BITS, NCH, NPASS> t[MAXK];
-#pragma unroll
-  for (int k = 0; k < MAXK; ++k) {
-    if (k < p.K) {  // wave-uniform
-      const bool v = ids[k] >= 0 && ids[k] < p.E;
-      down_load(t[k], p.experts + (size_t)(v ? ids[k] : 0) * p.stride, p.off, p.H, m, row0);
-    }
   }
   DnTile<BITS, NCH, NPASS> ts;
   if constexpr (SHARED_IN) down_load(ts, p.shared_rec, p.soff, p.H, m, row0);
   const int lds_stride = (p.I / NC) * (NC + kLdsPad);  // floats per expert in LDS
+  // float4 per thread held in registers (8192 values); the rest, if any, go
+  // through a plain loop after the barrier's other loads
+  constexpr int kHRegs = 8;
+  float4 hv[kHRegs];
+  const int nh = (p.K + (SHARED_IN ? 1 : 0)) * p.I;
+  const int nr = p.K * p.I;
   if constexpr (USE_LDS) {
-    const int nh = (p.K + (SHARED_IN ? 1 : 0)) * p.I;
-    const int nr = p.K * p.I;
-    for (int e = threadIdx.x * 4; e < nh; e += kBlock * 4) {
+    // branch-free: positions past the end load element 0 and are not stored
+#pragma unroll
+    for (int i = 0; i < kHRegs; ++i) {
+      const int e0 = (i * kBlock + threadIdx.x) * 4;
+      const int e = e0 < nh ? e0 : 0;
+      const float *src = e < nr ? p.h_routed + e : p.h_shared + (e - nr);
+      hv[i] = *reinterpret_cast<const float4 *>(src);
+    }
+  }
+  DnTile<BITS, NCH, NPASS> t[MAXK];
+#pragma unroll
+  for (int k = 0; k < MAXK; ++k) {
+    if (k < p.K) {  // wave-uniform
+      ids[k] = wave_uniform(ids[k]);
+      const bool v = ids[k] >= 0 && ids[k] < p.E;
+      down_load(t[k], p.experts + (size_t)(v ? ids[k] : 0) * p.stride, p.off, p.H, m, row0);
+    }
+  }
+  if constexpr (USE_LDS) {
+    // expert of element e: (e + 0.5) / I rounded down, exact in fp32 here
+    // (e < 2^17 and the quotient stays at least 0.5 / I from an integer)
+    const float inv_i = 1.0f / (float)p.I;
+#pragma unroll
+    for (int i = 0; i < kHRegs; ++i) {
+      const int e = (i * kBlock + threadIdx.x) * 4;
+      if (e < nh) {
+        const int k = (int)(((float)e + 0.5f) * inv_i);
+        const int col = e - k * p.I;
+        const int chunk = col / NC;  // NC is a power of two
+        *reinterpret_cast<float4 *>(hl + k * lds_stride + chunk * (NC + kLdsPad) + (col - chunk * NC)) = hv[i];
+      }
+    }
+    for (int e = (kHRegs * kBlock + threadIdx.x) * 4; e < nh; e += kBlock * 4) {
       const float4 v = e < nr ? *reinterpret_cast<const float4 *>(p.h_routed + e)
                               : *reinterpret_cast<const float4 *>(p.h_shared + (e - nr));
-      const int k = e / p.I, col = e - k * p.I;
+      const int k = (int)(((float)e + 0.5f) * inv_i);
+      const int col = e - k * p.I;
       const int chunk = col / NC;
       *reinterpret_cast<float4 *>(hl + k * lds_stride + chunk * (NC + kLdsPad) + (col - chunk * NC)) = v;
     }
@@ -1036,6 +1068,9 @@ __global__ __launch_bounds__(kBlock) void k_down_combine(DownParams p) {
   float acc[NPASS];
 #pragma unroll
   for (int i = 0; i < NPASS; ++i) acc[i] = 0.f;
+  const float sig = p.sigma[0];
+  if constexpr (SHARED_IN)
+    down_accumulate<BITS, NCH, NPASS, XSH>(hs, m, p.H, row0, true, sig, ts, acc);
 #pragma unroll
   for (int k = 0; k < MAXK; ++k) {
     if (k < p.K) {
@@ -1043,9 +1078,6 @@ __global__ __launch_bounds__(kBlock) void k_down_combine(DownParams p) {
       down_accumulate<BITS, NCH, NPASS, XSH>(hr + (size_t)k * hstride, m, p.H, row0, v, wk[k], t[k], acc);
     }
   }
-  const float sig = p.sigma[0];
-  if constexpr (SHARED_IN)
-    down_accumulate<BITS, NCH, NPASS, XSH>(hs, m, p.H, row0, true, sig, ts, acc);
 #pragma unroll
   for (int i = 0; i < NPASS; ++i) {
     const float s = seg_sum(acc[i], m.lg);
@@ -1397,7 +1429,7 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
   const int bits = p.bits_r;
   const int nch = nch_for(p.I, bits);
   const int rpp = rpp_for(p.I, bits);
-  const int npass = clamp_pass(nch, pick_pass(tune().dn, rpp >= 4 ? 1 : (rpp >= 2 ? 2 : 4)));
+  const int npass = clamp_pass(nch, pick_pass(tune().dn, rpp >= 2 ? 1 : 2));
   p.rows_per_wave = npass * rpp;
   if (p.combine) {
     const bool shared_in = p.h_shared != nullptr;
