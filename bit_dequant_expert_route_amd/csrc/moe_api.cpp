@@ -206,8 +206,11 @@ int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in
   float *y_shared = reinterpret_cast<float *>(ws + wl.y_shared);
   float *x_stage = reinterpret_cast<float *>(ws + wl.x_stage);
   float *hres_stage = reinterpret_cast<float *>(ws + wl.hres_stage);
-  uint32_t *xs_pairs = xsrc == XS_BF16 ? reinterpret_cast<uint32_t *>(ws + wl.xs_pairs) : nullptr;
-  float *xs_sums = xsrc == XS_BF16 ? reinterpret_cast<float *>(ws + wl.xs_sums) : nullptr;
+  // each gate/up wave stages its chunks of x from x itself: reading the
+  // input is faster than waiting for a staging buffer the router kernel has
+  // just written (data written by the previous kernel come from memory)
+  uint32_t *xs_pairs = nullptr;
+  float *xs_sums = nullptr;
 
   // K1
   HeadParams hp = head_params(L, 1);

@@ -316,6 +316,27 @@ __device__ __forceinline__ XRaw<BITS, XS> load_raw(const void *x, const float *x
 
 template <int BITS, int XS>
 __device__ __forceinline__ XStage<BITS, XS != XS_BF16> stage_raw(const XRaw<BITS, XS> &r) {
+  if constexpr (BITS == 4 && XS == XS_BF16) {
+    // bf16 x, 4-bit codes: pair 4t + n = (x[8t + n], x[8t + 4 + n]) is two
+    // bf16 halves of the loaded words, gathered by one byte permute; the
+    // sum of x is the constant part of the codes divided by 16 (exact
+    // scaling of the same fp32 sum)
+    XStage<4, false> s;
+    float off = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint4 u = r.u[t];
+      s.p[4 * t + 0] = __builtin_amdgcn_perm(u.z, u.x, 0x05040100u);
+      s.p[4 * t + 1] = __builtin_amdgcn_perm(u.z, u.x, 0x07060302u);
+      s.p[4 * t + 2] = __builtin_amdgcn_perm(u.w, u.y, 0x05040100u);
+      s.p[4 * t + 3] = __builtin_amdgcn_perm(u.w, u.y, 0x07060302u);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) off = dot2bf(kMagic16, s.p[4 * t + n], off);
+    }
+    s.off = off;
+    s.xs = off * 0.0625f;
+    return s;
+  }
   float v[ChunkGeom<BITS>::kCols];
 #pragma unroll
   for (int i = 0; i < XRaw<BITS, XS>::kN; ++i) {
@@ -485,10 +506,27 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
-// the logits of one token, one register per 64 experts
+// The logits of one token.  E <= 512: lane l holds experts 8l .. 8l+7 in
+// v[0..7] (contiguous, for the lane-sort selection below); otherwise one
+// register per 64 experts (expert 64 i + l in v[i]).
 __device__ __forceinline__ void topk_load(const float *__restrict__ lg, int E,
                                           float (&v)[kTopkNpl]) {
   const int lane = lane_id();
+  if (E <= 512) {  // wave-uniform
+    const int e0 = lane * 8;
+    if ((E & 7) == 0) {
+      const float4 *q = reinterpret_cast<const float4 *>(lg + (e0 < E ? e0 : 0));
+      const float4 a = q[0], b = q[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = lg[e0 + i < E ? e0 + i : 0];
+    }
+#pragma unroll
+    for (int i = 8; i < kTopkNpl; ++i) v[i] = -INFINITY;
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kTopkNpl; ++i) {
     const int e = i * 64 + lane;
@@ -550,10 +588,100 @@ __device__ __forceinline__ void topk_select_n(float (&v)[kTopkNpl], int K, int r
   w_out = mine ? t / den : __builtin_nanf("");
 }
 
+// Order-preserving unsigned key of a logit: larger logit, larger key.  NaN
+// maps to the key of -inf and -0 to that of +0, so that logits equal as
+// floats get equal keys.
+__device__ __forceinline__ uint32_t logit_key(float f) {
+  f = __builtin_isnan(f) ? -INFINITY : f + 0.0f;
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  // every lane of each 16-lane row now holds its row's maximum
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// E <= 512 (lane-contiguous layout of topk_load).  Each logit becomes the
+// 64-bit word (key << 32) | (2^32 - 1 - expert): a larger word is a larger
+// logit, or an equal logit with a lower expert.  Every lane sorts its 8 words
+// with a 19-comparator, depth-6 sorting network; each of the K rounds is then
+// a wave maximum of the lanes' first keys, the lowest lane holding it (lanes
+// own increasing expert ranges, so that is the lowest expert among equal
+// logits) and a shift of that lane's list.
+__device__ __forceinline__ void topk_select8(float (&v)[kTopkNpl], int E, int K, int renorm,
+                                             int &e_out, float &w_out) {
+  const int lane = lane_id();
+  uint64_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = lane * 8 + i;
+    c[i] = e < E ? ((uint64_t)logit_key(v[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
+    v[i] = e < E ? key_logit(logit_key(v[i])) : -INFINITY;  // for the softmax denominator
+  }
+#define MOE_CX(i, j)                          \
+  do {                                        \
+    const bool sw_ = c[j] > c[i];             \
+    const uint64_t t_ = sw_ ? c[j] : c[i];    \
+    c[j] = sw_ ? c[i] : c[j];                 \
+    c[i] = t_;                                \
+  } while (0)
+  MOE_CX(0, 2); MOE_CX(1, 3); MOE_CX(4, 6); MOE_CX(5, 7);
+  MOE_CX(0, 4); MOE_CX(1, 5); MOE_CX(2, 6); MOE_CX(3, 7);
+  MOE_CX(0, 1); MOE_CX(2, 3); MOE_CX(4, 5); MOE_CX(6, 7);
+  MOE_CX(2, 4); MOE_CX(3, 5);
+  MOE_CX(1, 4); MOE_CX(3, 6);
+  MOE_CX(1, 2); MOE_CX(3, 4); MOE_CX(5, 6);
+#undef MOE_CX
+  uint32_t my_k = 0;
+  int my_e = -2;
+  uint32_t k0 = 0;
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    const uint32_t m = wave_max_u32((uint32_t)(c[0] >> 32));
+    const uint64_t b = __ballot((uint32_t)(c[0] >> 32) == m);
+    const int src = __builtin_ctzll(b);  // b != 0: m is some lane's key
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)c[0], src);
+    const uint32_t ex = 0xFFFFFFFFu - lo;
+    const int sel = (m != 0 && ex < (uint32_t)E) ? (int)ex : -2;
+    if (lane == src) {  // shift the winner's list
+#pragma unroll
+      for (int i = 0; i < 7; ++i) c[i] = c[i + 1];
+      c[7] = 0ull;
+    }
+    if (lane == k) {
+      my_k = m;
+      my_e = sel;
+    }
+    if (k == 0) k0 = m;
+  }
+  const float mx = key_logit(k0);
+  const bool mine = lane < K && my_e >= 0;
+  const float t = mine ? expf(key_logit(my_k) - mx) : 0.f;
+  float z = t;
+  if (!renorm) {
+    z = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z += expf(v[i] - mx);
+  }
+  const float den = seg_sum(z, 6);
+  e_out = my_e;
+  w_out = mine ? t / den : __builtin_nanf("");
+}
+
 __device__ __forceinline__ void topk_select(float (&v)[kTopkNpl], int E, int K, int renorm,
                                             int &e_out, float &w_out) {
-  static_assert(kTopkNpl == 16, "two register counts below");
-  if (E <= 512) topk_select_n<8>(v, K, renorm, e_out, w_out);
+  static_assert(kTopkNpl == 16, "expert registers of the wide layout");
+  if (E <= 512) topk_select8(v, E, K, renorm, e_out, w_out);
   else topk_select_n<16>(v, K, renorm, e_out, w_out);
 }
 
@@ -736,10 +864,7 @@ __device__ __forceinline__ void write_xstage(const void *x, int H, uint32_t *pai
   constexpr int NP = ChunkGeom<BITS>::kPairs;
   const int cpr = H / ChunkGeom<BITS>::kCols;
   for (int c = lane_id(); c < cpr; c += 64) {
-    XStage<BITS, false> s;
-    float v[ChunkGeom<BITS>::kCols];
-    load_x_chunk<BITS, XS_BF16>(x, nullptr, c * ChunkGeom<BITS>::kCols, v);
-    stage_chunk<BITS>(v, s);
+    const XStage<BITS, false> s = make_stage<BITS, XS_BF16>(x, nullptr, c);
     uint4 *pp = reinterpret_cast<uint4 *>(pairs + (size_t)c * NP);
 #pragma unroll
     for (int i = 0; i < NP / 4; ++i)
@@ -892,7 +1017,11 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
       if (wv == 0) {
         int e;
         float w;
+        // the selection gates every routed load of the workgroup: issue it
+        // ahead of the shared-expert waves computing on the same SIMD
+        __builtin_amdgcn_s_setprio(3);
         topk_select(lv, p.E, p.K, p.renorm, e, w);
+        __builtin_amdgcn_s_setprio(0);
         if (blk == p.n_shared_blocks) topk_store(e, w, p.K, p.idx_out, p.w_out);
         if (lane_id() < p.K) sel_ids[lane_id()] = e;
       }
