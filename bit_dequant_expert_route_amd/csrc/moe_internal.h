@@ -108,7 +108,8 @@ struct GroupedParams {
   // down outputs
   float *y_routed;                // [T K][H] by pair
   float *y_shared;                // [T][H]
-  int rows_per_wave, tiles;       // set by the launcher
+  int rows_per_wave, tiles;       // set by the launcher (tiles of four waves)
+  int tok_batch;                  // tokens staged in LDS at a time (launcher)
 };
 hipError_t launch_gateup_grouped(const GroupedParams &p, hipStream_t s);
 hipError_t launch_down_grouped(const GroupedParams &p, hipStream_t s);

@@ -1077,17 +1077,11 @@ __device__ __forceinline__ void down_load(DnTile<BITS, NCH, NPASS> &t, const uin
 
 // weighted partial sums of one expert into acc[p]; the passes are taken in
 // pairs so that two rows form independent accumulation chains
-template <int BITS, int NCH, int NPASS, int XS>
-__device__ __forceinline__ void down_accumulate(const float *hin, const RowMap &m, int H,
-                                                int row0, bool valid, float wgt,
-                                                const DnTile<BITS, NCH, NPASS> &t,
-                                                float (&acc)[NPASS]) {
-  XStage<BITS, true> xs[NCH];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = m.li + (j << m.lg);
-    xs[j] = make_stage<BITS, XS>(hin, hin, c < m.cpr ? c : 0);
-  }
+template <int BITS, int NCH, int NPASS>
+__device__ __forceinline__ void down_accumulate_staged(const XStage<BITS, true> (&xs)[NCH],
+                                                       const RowMap &m, int H, int row0, bool valid,
+                                                       float wgt, const DnTile<BITS, NCH, NPASS> &t,
+                                                       float (&acc)[NPASS]) {
 #pragma unroll
   for (int p = 0; p < NPASS; p += 2) {
     constexpr int kLast = NPASS - 1;
@@ -1105,6 +1099,20 @@ __device__ __forceinline__ void down_accumulate(const float *hin, const RowMap &
     acc[p] = valid ? fmaf(wgt, part0, acc[p]) : __builtin_nanf("");
     if (p1 != p) acc[p1] = valid ? fmaf(wgt, part1, acc[p1]) : __builtin_nanf("");
   }
+}
+
+template <int BITS, int NCH, int NPASS, int XS>
+__device__ __forceinline__ void down_accumulate(const float *hin, const RowMap &m, int H,
+                                                int row0, bool valid, float wgt,
+                                                const DnTile<BITS, NCH, NPASS> &t,
+                                                float (&acc)[NPASS]) {
+  XStage<BITS, true> xs[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = m.li + (j << m.lg);
+    xs[j] = make_stage<BITS, XS>(hin, hin, c < m.cpr ? c : 0);
+  }
+  down_accumulate_staged<BITS, NCH, NPASS>(xs, m, H, row0, valid, wgt, t, acc);
 }
 
 // COMBINE: out = h_res + sum_k w_k y_k + sigma * y_shared for rows of a wave
@@ -1256,14 +1264,16 @@ __global__ __launch_bounds__(kBlock) void k_down_y(DownParams p) {
 // then a counting sort of the T*K (token, expert) pairs by expert id with the
 // pair order kept inside an expert.  P = T*K <= 512 and the ranks are plain
 // counts over the pairs, so the result does not depend on thread timing.
-__global__ __launch_bounds__(kBlock) void k_route_group(RouteGroupParams p) {
+constexpr int kGroupBlock = 1024;  // one wave per token for up to 16 tokens at a time
+
+__global__ __launch_bounds__(kGroupBlock) void k_route_group(RouteGroupParams p) {
   __shared__ int pe[kMaxTokens * kMaxK];
   __shared__ int pless[kMaxTokens * kMaxK];
   __shared__ unsigned char pfirst[kMaxTokens * kMaxK];
   __shared__ int n_first;
   const int wv = threadIdx.x >> 6, lane = lane_id();
   if (threadIdx.x == 0) n_first = 0;
-  for (int t = wv; t < p.T; t += kBlock / 64) {
+  for (int t = wv; t < p.T; t += kGroupBlock / 64) {
     float v[kTopkNpl];
     topk_load(p.logits + (size_t)t * p.E, p.E, v);
     int e;
@@ -1275,7 +1285,7 @@ __global__ __launch_bounds__(kBlock) void k_route_group(RouteGroupParams p) {
   __syncthreads();
   const int P = p.T * p.K;
   int mine = 0;
-  for (int q = threadIdx.x; q < P; q += kBlock) {
+  for (int q = threadIdx.x; q < P; q += kGroupBlock) {
     const int e = pe[q];
     int less = 0, before = 0;
     for (int r = 0; r < P; ++r) {
@@ -1290,7 +1300,7 @@ __global__ __launch_bounds__(kBlock) void k_route_group(RouteGroupParams p) {
   }
   atomicAdd(&n_first, mine);
   __syncthreads();
-  for (int q = threadIdx.x; q < P; q += kBlock) {
+  for (int q = threadIdx.x; q < P; q += kGroupBlock) {
     if (!pfirst[q]) continue;
     const int e = pe[q];
     int g = 0;
@@ -1330,88 +1340,203 @@ __device__ __forceinline__ GroupRef group_ref(const GroupedParams &p, int g, int
   return r;
 }
 
-template <int BITS, int NCH, int XS>
-__device__ __forceinline__ void group_stage(const GroupedParams &p, const RowMap &m, int tok,
-                                            XStage<BITS, XS != XS_BF16> (&xs)[NCH]) {
+// ---- staged activations in LDS, shared by the workgroup's four waves ----
+// A chunk's LDS slot: its stage's words rounded up to a multiple of 4 and, if
+// that count of 16-byte units is even, one unit more, so that lanes reading
+// consecutive chunks start in different bank groups.
+template <typename Stage>
+__host__ __device__ constexpr int lds_chunk_words() {
+  constexpr int n = ((int)(sizeof(Stage) / 4) + 3) / 4 * 4;
+  return (n / 4) % 2 == 0 ? n + 4 : n;
+}
+
+template <int BITS>
+__device__ __forceinline__ void lds_store(uint32_t *d, const XStage<BITS, false> &s) {
+  constexpr int NP = ChunkGeom<BITS>::kPairs;
 #pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c0 = m.li + (j << m.lg);
-    const int c = c0 < m.cpr ? c0 : 0;
-    if constexpr (XS == XS_BF16) {
-      if (p.xs_pairs) {
-        xs[j] = read_stage<BITS>(p.xs_pairs + (size_t)tok * p.xs_pair_stride,
-                                 p.xs_sums + (size_t)tok * p.xs_sum_stride, c);
-        continue;
-      }
-    }
-    const void *xt = XS == XS_BF16
-                         ? static_cast<const void *>(static_cast<const uint16_t *>(p.x) + (size_t)tok * p.H)
-                         : static_cast<const void *>(static_cast<const float *>(p.x) + (size_t)tok * p.H);
-    xs[j] = make_stage<BITS, XS>(xt, nullptr, c);
+  for (int i = 0; i < NP / 4; ++i)
+    reinterpret_cast<uint4 *>(d)[i] = make_uint4(s.p[4 * i], s.p[4 * i + 1], s.p[4 * i + 2], s.p[4 * i + 3]);
+  *reinterpret_cast<float2 *>(d + NP) = make_float2(s.off, s.xs);
+}
+template <int BITS>
+__device__ __forceinline__ void lds_load(const uint32_t *d, XStage<BITS, false> &s) {
+  constexpr int NP = ChunkGeom<BITS>::kPairs;
+#pragma unroll
+  for (int i = 0; i < NP / 4; ++i) {
+    const uint4 u = reinterpret_cast<const uint4 *>(d)[i];
+    s.p[4 * i] = u.x;
+    s.p[4 * i + 1] = u.y;
+    s.p[4 * i + 2] = u.z;
+    s.p[4 * i + 3] = u.w;
+  }
+  const float2 t = *reinterpret_cast<const float2 *>(d + NP);
+  s.off = t.x;
+  s.xs = t.y;
+}
+template <int BITS>
+__device__ __forceinline__ void lds_store(uint32_t *d, const XStage<BITS, true> &s) {
+  constexpr int NC = ChunkGeom<BITS>::kCols;
+#pragma unroll
+  for (int i = 0; i < NC / 4; ++i)
+    reinterpret_cast<float4 *>(d)[i] = make_float4(s.v[4 * i], s.v[4 * i + 1], s.v[4 * i + 2], s.v[4 * i + 3]);
+  reinterpret_cast<float *>(d)[NC] = s.xs;
+}
+template <int BITS>
+__device__ __forceinline__ void lds_load(const uint32_t *d, XStage<BITS, true> &s) {
+  constexpr int NC = ChunkGeom<BITS>::kCols;
+#pragma unroll
+  for (int i = 0; i < NC / 4; ++i) {
+    const float4 u = reinterpret_cast<const float4 *>(d)[i];
+    s.v[4 * i] = u.x;
+    s.v[4 * i + 1] = u.y;
+    s.v[4 * i + 2] = u.z;
+    s.v[4 * i + 3] = u.w;
+  }
+  s.xs = reinterpret_cast<const float *>(d)[NC];
+}
+
+// stage chunk c of token tok's x (from the staged buffer when there is one)
+template <int BITS, int XS>
+__device__ __forceinline__ XStage<BITS, XS != XS_BF16> group_stage_chunk(const GroupedParams &p,
+                                                                         int tok, int c) {
+  if constexpr (XS == XS_BF16) {
+    if (p.xs_pairs)
+      return read_stage<BITS>(p.xs_pairs + (size_t)tok * p.xs_pair_stride,
+                              p.xs_sums + (size_t)tok * p.xs_sum_stride, c);
+    return make_stage<BITS, XS>(static_cast<const uint16_t *>(p.x) + (size_t)tok * p.H, nullptr, c);
+  } else {
+    return make_stage<BITS, XS>(static_cast<const float *>(p.x) + (size_t)tok * p.H, nullptr, c);
   }
 }
 
+// Work items are (group, block tile): the workgroup's four waves take
+// consecutive row tiles of one expert group, so the tokens' activations are
+// staged into LDS once per workgroup, tok_batch tokens at a time, and read
+// there by all four waves.
 template <int BITS, int NCH, int NPASS, int XS>
 __global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedParams p) {
+  extern __shared__ uint32_t lds_x[];
   constexpr bool XF32 = XS != XS_BF16;
-  const int wave = wave_uniform(blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6));
-  const int nw = gridDim.x * (kBlock / 64);
+  using Stage = XStage<BITS, XF32>;
+  constexpr int CS = lds_chunk_words<Stage>();
+  const int wv = wave_uniform(threadIdx.x >> 6);
   const int U = p.do_routed ? wave_uniform(p.g_count[0]) : 0;
   const int n_items = (U + (p.do_shared ? 1 : 0)) * p.tiles;
   const RowMap m = row_map<BITS>(p.H);
-  for (int item = wave; item < n_items; item += nw) {
-    const int g = item / p.tiles;
-    const int row0 = (item - g * p.tiles) * p.rows_per_wave;
-    const GroupRef gr = group_ref(p, g, U);
+  const int cpr = m.cpr;
+  // the next item's weight rows are requested before this item's tokens are
+  // worked through
+  GUTile<BITS, NCH, NPASS> next;
+  GroupRef ngr;
+  int nrow0 = 0;
+  auto fetch = [&](int item, GUTile<BITS, NCH, NPASS> &t, GroupRef &r, int &row0) {
+    const int g = item < n_items ? item / p.tiles : 0;
+    row0 = ((item - g * p.tiles) * 4 + wv) * p.rows_per_wave;
+    r = group_ref(p, g, U);
+    const bool v = r.shared ? true : (r.id >= 0 && r.id < p.E);
+    const uint8_t *rec = r.shared ? p.shared_rec : p.experts + (size_t)(v ? r.id : 0) * p.stride;
+    gu_load(t, rec, r.shared ? p.soff : p.off, m, p.I, row0);
+  };
+  if (blockIdx.x < n_items) fetch(blockIdx.x, next, ngr, nrow0);
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const GUTile<BITS, NCH, NPASS> tile = next;
+    const GroupRef gr = ngr;
+    const int row0 = nrow0;
+    if (item + (int)gridDim.x < n_items) fetch(item + gridDim.x, next, ngr, nrow0);
     const bool valid = gr.shared ? true : (gr.id >= 0 && gr.id < p.E);
-    const uint8_t *rec = gr.shared ? p.shared_rec : p.experts + (size_t)(valid ? gr.id : 0) * p.stride;
-    GUTile<BITS, NCH, NPASS> tile;
-    gu_load(tile, rec, gr.shared ? p.soff : p.off, m, p.I, row0);
-    // tokens of the group, the next token's x staged while this one computes
-    XStage<BITS, XF32> cur[NCH];
-    group_stage<BITS, NCH, XS>(p, m, __builtin_amdgcn_readlane(gr.tok, 0), cur);
-    for (int i = 0; i < gr.n; ++i) {
-      const int pair = __builtin_amdgcn_readlane(gr.pair, i);
-      const int tok = __builtin_amdgcn_readlane(gr.tok, i);
-      XStage<BITS, XF32> nxt[NCH];
-      if (i + 1 < gr.n) group_stage<BITS, NCH, XS>(p, m, __builtin_amdgcn_readlane(gr.tok, i + 1), nxt);
-      float *hout = gr.shared ? p.h_shared + (size_t)tok * p.I : p.h_routed + (size_t)pair * p.I;
-      gu_compute(tile, cur, m, p.I, row0, valid, hout);
+    for (int i0 = 0; i0 < gr.n; i0 += p.tok_batch) {
+      const int nb = gr.n - i0 < p.tok_batch ? gr.n - i0 : p.tok_batch;
+      __syncthreads();  // the previous batch has been read
+      // the trip count is the same for every thread, so every lane is active
+      // at the shuffle (a lane cannot read an inactive lane's register)
+      for (int base = 0; base < nb * cpr; base += kBlock) {
+        const int idx = base + threadIdx.x;
+        const int b = idx / cpr, c = idx - b * cpr;
+        const int tok = __shfl(gr.tok, (i0 + b) & 63, 64);
+        if (idx < nb * cpr)
+          lds_store<BITS>(lds_x + (size_t)(b * cpr + c) * CS, group_stage_chunk<BITS, XS>(p, tok, c));
+      }
+      __syncthreads();
+      for (int b = 0; b < nb; ++b) {
+        Stage xs[NCH];
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) cur[j] = nxt[j];
+        for (int j = 0; j < NCH; ++j) {
+          const int c0 = m.li + (j << m.lg);
+          lds_load<BITS>(lds_x + (size_t)(b * cpr + (c0 < cpr ? c0 : 0)) * CS, xs[j]);
+        }
+        const int pair = __builtin_amdgcn_readlane(gr.pair, i0 + b);
+        const int tok = __builtin_amdgcn_readlane(gr.tok, i0 + b);
+        float *hout = gr.shared ? p.h_shared + (size_t)tok * p.I : p.h_routed + (size_t)pair * p.I;
+        gu_compute(tile, xs, m, p.I, row0, valid, hout);
+      }
     }
   }
 }
 
+// down projection over the groups; the SwiGLU outputs of a batch of tokens
+// go to LDS (padded per code chunk) once per workgroup
 template <int BITS, int NCH, int NPASS>
 __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedParams p) {
-  const int wave = wave_uniform(blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6));
-  const int nw = gridDim.x * (kBlock / 64);
+  extern __shared__ float lds_h[];
+  constexpr int NC = ChunkGeom<BITS>::kCols;
+  constexpr int PC = NC + kLdsPad;
+  const int wv = wave_uniform(threadIdx.x >> 6);
   const int U = p.do_routed ? wave_uniform(p.g_count[0]) : 0;
   const int n_items = (U + (p.do_shared ? 1 : 0)) * p.tiles;
   const RowMap m = row_map<BITS>(p.I);
-  for (int item = wave; item < n_items; item += nw) {
-    const int g = item / p.tiles;
-    const int row0 = (item - g * p.tiles) * p.rows_per_wave;
-    const GroupRef gr = group_ref(p, g, U);
+  const int tok_floats = (p.I / NC) * PC;
+  DnTile<BITS, NCH, NPASS> next;
+  GroupRef ngr;
+  int nrow0 = 0;
+  auto fetch = [&](int item, DnTile<BITS, NCH, NPASS> &t, GroupRef &r, int &row0) {
+    const int g = item < n_items ? item / p.tiles : 0;
+    row0 = ((item - g * p.tiles) * 4 + wv) * p.rows_per_wave;
+    r = group_ref(p, g, U);
+    const bool v = r.shared ? true : (r.id >= 0 && r.id < p.E);
+    const uint8_t *rec = r.shared ? p.shared_rec : p.experts + (size_t)(v ? r.id : 0) * p.stride;
+    down_load(t, rec, r.shared ? p.soff : p.off, p.H, m, row0);
+  };
+  if (blockIdx.x < n_items) fetch(blockIdx.x, next, ngr, nrow0);
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const DnTile<BITS, NCH, NPASS> tile = next;
+    const GroupRef gr = ngr;
+    const int row0 = nrow0;
+    if (item + (int)gridDim.x < n_items) fetch(item + gridDim.x, next, ngr, nrow0);
     const bool valid = gr.shared ? true : (gr.id >= 0 && gr.id < p.E);
-    const uint8_t *rec = gr.shared ? p.shared_rec : p.experts + (size_t)(valid ? gr.id : 0) * p.stride;
-    DnTile<BITS, NCH, NPASS> tile;
-    down_load(tile, rec, gr.shared ? p.soff : p.off, p.H, m, row0);
-    for (int i = 0; i < gr.n; ++i) {
-      const int pair = __builtin_amdgcn_readlane(gr.pair, i);
-      const int tok = __builtin_amdgcn_readlane(gr.tok, i);
-      const float *hin = gr.shared ? p.h_shared + (size_t)tok * p.I : p.h_routed + (size_t)pair * p.I;
-      float *yout = gr.shared ? p.y_shared + (size_t)tok * p.H : p.y_routed + (size_t)pair * p.H;
-      float acc[NPASS];
+    for (int i0 = 0; i0 < gr.n; i0 += p.tok_batch) {
+      const int nb = gr.n - i0 < p.tok_batch ? gr.n - i0 : p.tok_batch;
+      __syncthreads();  // the previous batch has been read
+      for (int b = 0; b < nb; ++b) {
+        const int pair = __builtin_amdgcn_readlane(gr.pair, i0 + b);
+        const int tok = __builtin_amdgcn_readlane(gr.tok, i0 + b);
+        const float *hin = gr.shared ? p.h_shared + (size_t)tok * p.I : p.h_routed + (size_t)pair * p.I;
+        for (int col = threadIdx.x * 4; col < p.I; col += kBlock * 4) {
+          const int chunk = col / NC;
+          *reinterpret_cast<float4 *>(lds_h + b * tok_floats + chunk * PC + (col - chunk * NC)) =
+              *reinterpret_cast<const float4 *>(hin + col);
+        }
+      }
+      __syncthreads();
+      for (int b = 0; b < nb; ++b) {
+        const int pair = __builtin_amdgcn_readlane(gr.pair, i0 + b);
+        const int tok = __builtin_amdgcn_readlane(gr.tok, i0 + b);
+        float *yout = gr.shared ? p.y_shared + (size_t)tok * p.H : p.y_routed + (size_t)pair * p.H;
+        XStage<BITS, true> xs[NCH];
 #pragma unroll
-      for (int k = 0; k < NPASS; ++k) acc[k] = 0.f;
-      down_accumulate<BITS, NCH, NPASS, XS_F32>(hin, m, p.H, row0, valid, 1.0f, tile, acc);
+        for (int j = 0; j < NCH; ++j) {
+          const int c = m.li + (j << m.lg);
+          xs[j] = make_stage<BITS, XS_LDSPAD>(nullptr, lds_h + b * tok_floats, c < m.cpr ? c : 0);
+        }
+        float acc[NPASS];
 #pragma unroll
-      for (int k = 0; k < NPASS; ++k) {
-        const float sum = seg_sum(acc[k], m.lg);
-        const int r = row0 + k * m.rpp + m.rip;
-        if (m.li == 0 && r < p.H) yout[r] = sum;
+        for (int k = 0; k < NPASS; ++k) acc[k] = 0.f;
+        down_accumulate_staged<BITS, NCH, NPASS>(xs, m, p.H, row0, valid, 1.0f, tile, acc);
+#pragma unroll
+        for (int k = 0; k < NPASS; ++k) {
+          const float sum = seg_sum(acc[k], m.lg);
+          const int r = row0 + k * m.rpp + m.rip;
+          if (m.li == 0 && r < p.H) yout[r] = sum;
+        }
       }
     }
   }
@@ -1602,31 +1727,58 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
 }
 
 hipError_t launch_route_group(const RouteGroupParams &p, hipStream_t s) {
-  MOE_LAUNCH(k_route_group, dim3(1), dim3(kBlock), 0, s, p);
+  MOE_LAUNCH(k_route_group, dim3(1), dim3(kGroupBlock), 0, s, p);
   return hipGetLastError();
 }
 
-// work items = groups x row tiles, taken by a grid of at most 2048
-// workgroups in a strided loop
-static dim3 grouped_grid(const GroupedParams &p) {
+// block tiles of four waves; a grid of at most 512 (gate/up) or 768 (down)
+// workgroups, what the kernels' register use lets a CU hold, takes the work
+// items in a strided loop; LDS holds up to 48 KiB of staged activations
+#define MOE_DISPATCH_G(nch, npass, ...)                                                  \
+  do {                                                                                   \
+    if (nch == 1 && npass == 1) { constexpr int NCH_ = 1, NP_ = 1; __VA_ARGS__; }        \
+    else if (nch == 1 && npass == 2) { constexpr int NCH_ = 1, NP_ = 2; __VA_ARGS__; }   \
+    else if (nch == 1) { constexpr int NCH_ = 1, NP_ = 4; __VA_ARGS__; }                 \
+    else if (nch == 2 && npass <= 2) { constexpr int NCH_ = 2, NP_ = 2; __VA_ARGS__; }   \
+    else if (nch == 2) { constexpr int NCH_ = 2, NP_ = 4; __VA_ARGS__; }                 \
+    else { constexpr int NCH_ = 4, NP_ = 1; __VA_ARGS__; }                              \
+  } while (0)
+
+static constexpr size_t kGroupedLds = 48 * 1024;
+
+static dim3 grouped_grid(const GroupedParams &p, long cap) {
   const int max_groups = (p.T * p.K < p.E ? p.T * p.K : p.E) + 1;
-  const long items = (long)max_groups * p.tiles;
-  long blocks = (items + 3) / 4;
-  if (blocks > 2048) blocks = 2048;
+  long blocks = (long)max_groups * p.tiles;
+  if (blocks > cap) blocks = cap;
   return dim3((unsigned)(blocks < 1 ? 1 : blocks));
+}
+
+static int tok_batch_for(size_t per_token, int T) {
+  long n = (long)(kGroupedLds / per_token);
+  if (n < 1) n = 1;
+  return (int)(n < T ? n : T);
 }
 
 hipError_t launch_gateup_grouped(const GroupedParams &p0, hipStream_t s) {
   GroupedParams p = p0;
   const int nch = nch_for(p.H, p.bits);
   const int rpp = rpp_for(p.H, p.bits);
-  const int npass = clamp_pass(nch, pick_pass(tune().gu, rpp >= 2 ? 1 : 2));
+  // two rows per wave at most for rows of two chunks per lane: two
+  // workgroups fit a CU
+  int npass = nch >= 4 ? 1 : (rpp >= 4 ? 1 : (rpp >= 2 ? 2 : 4));
+  if (nch >= 2 && npass > 2) npass = 2;
   p.rows_per_wave = npass * rpp;
-  p.tiles = (p.I + p.rows_per_wave - 1) / p.rows_per_wave;
-  const dim3 grid = grouped_grid(p);
-#define MOE_GG(BITS, XS)                                                                    \
-  MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_gateup_grouped<BITS, NCH_, NP_, XS>), grid,       \
-                                      dim3(kBlock), 0, s, p))
+  p.tiles = (p.I + 4 * p.rows_per_wave - 1) / (4 * p.rows_per_wave);
+  const dim3 grid = grouped_grid(p, 512);
+  const int cpr = p.H * p.bits / 128;
+#define MOE_GG(BITS, XS)                                                                       \
+  do {                                                                                         \
+    const size_t per_tok = (size_t)cpr * lds_chunk_words<XStage<BITS, XS != XS_BF16>>() * 4;   \
+    p.tok_batch = tok_batch_for(per_tok, p.T);                                                 \
+    const size_t lds = per_tok * p.tok_batch;                                                  \
+    MOE_DISPATCH_G(nch, npass, MOE_LAUNCH((k_gateup_grouped<BITS, NCH_, NP_, XS>), grid,        \
+                                          dim3(kBlock), lds, s, p));                           \
+  } while (0)
   if (p.bits == 4) {
     if (p.xsrc == XS_BF16) { MOE_GG(4, XS_BF16); } else { MOE_GG(4, XS_F32); }
   } else {
@@ -1640,14 +1792,18 @@ hipError_t launch_down_grouped(const GroupedParams &p0, hipStream_t s) {
   GroupedParams p = p0;
   const int nch = nch_for(p.I, p.bits);
   const int rpp = rpp_for(p.I, p.bits);
-  const int npass = clamp_pass(nch, pick_pass(tune().dn, rpp >= 4 ? 1 : (rpp >= 2 ? 2 : 4)));
+  const int npass = nch >= 4 ? 1 : (rpp >= 8 ? 1 : (rpp >= 4 ? 2 : 4));
   p.rows_per_wave = npass * rpp;
-  p.tiles = (p.H + p.rows_per_wave - 1) / p.rows_per_wave;
-  const dim3 grid = grouped_grid(p);
+  p.tiles = (p.H + 4 * p.rows_per_wave - 1) / (4 * p.rows_per_wave);
+  const dim3 grid = grouped_grid(p, 768);
+  const int nc = 128 / p.bits;
+  const size_t per_tok = (size_t)(p.I / nc) * (nc + kLdsPad) * 4;
+  p.tok_batch = tok_batch_for(per_tok, p.T);
+  const size_t lds = per_tok * p.tok_batch;
   if (p.bits == 4) {
-    MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_grouped<4, NCH_, NP_>), grid, dim3(kBlock), 0, s, p));
+    MOE_DISPATCH_G(nch, npass, MOE_LAUNCH((k_down_grouped<4, NCH_, NP_>), grid, dim3(kBlock), lds, s, p));
   } else {
-    MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_grouped<2, NCH_, NP_>), grid, dim3(kBlock), 0, s, p));
+    MOE_DISPATCH_G(nch, npass, MOE_LAUNCH((k_down_grouped<2, NCH_, NP_>), grid, dim3(kBlock), lds, s, p));
   }
   return hipGetLastError();
 }
