@@ -372,7 +372,16 @@ def main():
         per.setdefault(name, []).append(ms)
     kern_us = {k: float(np.mean(v) * 1000.0) for k, v in per.items()}
     dom = "gateup"
-    achieved = kb[dom] / (kern_us[dom] * 1e-6) / 1e9
+    dom_bytes = kb[dom]
+    dom_kernel = "k_gateup (shared + routed gate/up + SwiGLU)"
+    if cfg.n_tokens > 1:
+        # grouped gate/up: each distinct routed expert and the shared one once,
+        # the tokens' x and the SwiGLU outputs of every (token, expert) pair
+        H, I, T, K = cfg.hidden, cfg.inter, cfg.n_tokens, cfg.top_k
+        gu = 2 * (I * H * cfg.bits_routed // 8 + I * (H // 64) * 4)
+        dom_bytes = int(round((extra["distinct"] + 1) * gu + T * H * 2 + (T * K + T) * I * 4))
+        dom_kernel = "k_gateup_grouped (distinct routed + shared experts, all tokens)"
+    achieved = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
     traffic = traffic_from_profiles(args.workload, dom)
     descr = {
         "q4_layer": "MoE layer decode, batch 1",
@@ -401,10 +410,10 @@ def main():
         "effective_GBps": round(bytes_per_unit / (us_per_layer * 1e-6) / 1e9, 1),
         "pct_hbm_peak": round(100.0 * bytes_per_unit / (us_per_layer * 1e-6) / 1e9 / PEAK_GBPS, 2),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
-        "roofline": {"bound": "hbm", "kernel": "k_gateup (shared + routed gate/up + SwiGLU)",
+        "roofline": {"bound": "hbm", "kernel": dom_kernel,
                      "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-                     "bytes_per_launch": kb[dom]},
+                     "bytes_per_launch": dom_bytes},
         "cpu_baseline": None,
     }
     if not args.no_cpu:
