@@ -64,6 +64,9 @@ class Oracle:
         L.oracle_rmsnorm.argtypes = [_dp, C.c_int, C.c_double, _dp]
         L.oracle_bf16_to_f64.restype = C.c_double
         L.oracle_bf16_to_f64.argtypes = [C.c_uint16]
+        L.oracle_gdn_step.restype = None
+        L.oracle_gdn_step.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, _dp, _dp, _dp, _dp,
+                                      _dp, _dp, _dp]
         L.oracle_layer.restype = None
         L.oracle_layer.argtypes = [
             C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
@@ -151,6 +154,22 @@ class Oracle:
 
     def bf16_to_f64(self, bits: int) -> float:
         return float(self._L.oracle_bf16_to_f64(bits))
+
+    def gdn_step(self, q, k, v, alpha, beta, state):
+        """One gated delta-rule decode step for [n_seq][n_heads] heads:
+        S <- alpha S; u = S k; S <- S + beta (v - u) k^T; o = S q.  Returns
+        (new state, o); the inputs are not modified."""
+        q = np.ascontiguousarray(q, dtype=np.float64)
+        k = np.ascontiguousarray(k, dtype=np.float64)
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        S = np.array(state, dtype=np.float64, copy=True, order="C")
+        n_seq, n_heads, d_v, d_k = S.shape
+        assert q.shape == k.shape == (n_seq, n_heads, d_k) and v.shape == (n_seq, n_heads, d_v)
+        a = np.ascontiguousarray(alpha, dtype=np.float64).reshape(n_seq, n_heads)
+        b = np.ascontiguousarray(beta, dtype=np.float64).reshape(n_seq, n_heads)
+        o = np.empty((n_seq, n_heads, d_v))
+        self._L.oracle_gdn_step(n_seq, n_heads, d_k, d_v, q, k, v, a, b, S, o)
+        return S, o
 
     # -- composite -------------------------------------------------------
     def route(self, router, router_dtype, gate_vec, gate_dtype, x, top_k, renorm):

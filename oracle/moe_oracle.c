@@ -32,7 +32,11 @@
  *   - renormalising the K selected probabilities is a flag;
  *   - the shared expert is gated by the scalar sigmoid(g . x);
  *   - SwiGLU applies silu to the gate projection: h = silu(gate x) * (up x);
- *   - RMSNorm has unit weight and eps 1e-6.
+ *   - RMSNorm has unit weight and eps 1e-6;
+ *   - the linear-attention decode step is the gated delta rule in the order
+ *     of the pages' BLAS calls: scale the state, u = S k, S += beta (v - u) k^T,
+ *     o = S q, with q, k, v, alpha, beta given (their projections are not part
+ *     of this step).
  */
 #include <math.h>
 #include <stdint.h>
@@ -297,4 +301,48 @@ void oracle_layer(int hidden, int inter, int n_experts, int top_k,
                   h + (size_t)top_k * inter, y + (size_t)top_k * hidden);
     oracle_combine(hidden, top_k, h_res, y, w, y + (size_t)top_k * hidden,
                    *sigma, out);
+}
+
+/* ------------------------------------------------------------------ */
+/* gated delta-rule decode step (the linear-attention layers)          */
+/* ------------------------------------------------------------------ */
+/* [openclawradar] "Accelerate BLAS for linear attention" and [a2a-fr]
+ * "Technical deep dive / 4": each of the 64 heads keeps a 128x128 state
+ * matrix that the decode step updates with a scale (sscal), a matrix-vector
+ * product (sgemv) and a rank-1 update (sger).  Taken in that order, with the
+ * state S stored as d_v rows of d_k columns:
+ *     S <- alpha S;  u = S k;  S <- S + beta (v - u) k^T;  o = S q
+ * for every sequence and head (q, k: d_k; v, o: d_v; alpha, beta: scalars).
+ * The state is updated in place. */
+void oracle_gdn_step(int n_seq, int n_heads, int d_k, int d_v, const double *q,
+                     const double *k, const double *v, const double *alpha,
+                     const double *beta, double *state, double *out)
+{
+    for (int s = 0; s < n_seq; ++s) {
+        for (int h = 0; h < n_heads; ++h) {
+            const size_t sh = (size_t)s * n_heads + h;
+            double *S = state + sh * (size_t)d_v * d_k;
+            const double *qh = q + sh * d_k, *kh = k + sh * d_k, *vh = v + sh * d_v;
+            double *oh = out + sh * d_v;
+            const double a = alpha[sh], b = beta[sh];
+            /* sscal */
+            for (size_t i = 0; i < (size_t)d_v * d_k; ++i) S[i] *= a;
+            for (int i = 0; i < d_v; ++i) {
+                double *row = S + (size_t)i * d_k;
+                /* sgemv: u_i = sum_j S_ij k_j */
+                double u = 0.0;
+                for (int j = 0; j < d_k; ++j) u += row[j] * kh[j];
+                /* sger: S_ij += beta (v_i - u_i) k_j */
+                const double c = b * (vh[i] - u);
+                for (int j = 0; j < d_k; ++j) row[j] += c * kh[j];
+            }
+            /* sgemv: o_i = sum_j S_ij q_j */
+            for (int i = 0; i < d_v; ++i) {
+                const double *row = S + (size_t)i * d_k;
+                double o = 0.0;
+                for (int j = 0; j < d_k; ++j) o += row[j] * qh[j];
+                oh[i] = o;
+            }
+        }
+    }
 }

@@ -389,4 +389,71 @@ def pin_layer_zero_experts(orc):
     assert np.array_equal(a["out"], args["h_res"]) and not np.any(a["y"])
 
 
+# ----------------------------------------------------------------------------
+# gated delta-rule decode step
+# ----------------------------------------------------------------------------
+def _gdn_inputs(rng, n_seq=2, n_heads=3, d_k=8, d_v=6):
+    S = rng.standard_normal((n_seq, n_heads, d_v, d_k))
+    q = rng.standard_normal((n_seq, n_heads, d_k))
+    k = rng.standard_normal((n_seq, n_heads, d_k))
+    v = rng.standard_normal((n_seq, n_heads, d_v))
+    return S, q, k, v
+
+
+def pin_gdn_identity(orc):
+    """alpha = 1, beta = 0: the state is unchanged (exactly) and o = S q
+    (numpy matmul)."""
+    rng = np.random.default_rng(11)
+    S, q, k, v = _gdn_inputs(rng)
+    ones, zeros = np.ones(S.shape[:2]), np.zeros(S.shape[:2])
+    Sn, o = orc.gdn_step(q, k, v, ones, zeros, S)
+    assert np.array_equal(Sn, S)
+    assert np.allclose(o, np.einsum("shij,shj->shi", S, q), rtol=1e-13, atol=1e-13)
+
+
+def pin_gdn_column_write(orc):
+    """alpha = 1, beta = 1, k = e_j: column j of the state becomes v and the
+    other columns keep their values (the delta rule writes v at key j)."""
+    rng = np.random.default_rng(12)
+    S, q, _, v = _gdn_inputs(rng)
+    j = 5
+    k = np.zeros(q.shape)
+    k[..., j] = 1.0
+    Sn, o = orc.gdn_step(q, k, v, np.ones(S.shape[:2]), np.ones(S.shape[:2]), S)
+    others = [c for c in range(S.shape[3]) if c != j]
+    assert np.array_equal(Sn[..., others], S[..., others])
+    assert np.allclose(Sn[..., j], v, rtol=0, atol=1e-15)
+    assert np.allclose(o, np.einsum("shij,shj->shi", Sn, q), rtol=1e-13, atol=1e-13)
+
+
+def pin_gdn_reset(orc):
+    """alpha = 0: the old state is forgotten, S = beta v k^T and o = beta v (k . q)."""
+    rng = np.random.default_rng(13)
+    S, q, k, v = _gdn_inputs(rng)
+    beta = rng.uniform(0.1, 0.9, S.shape[:2])
+    Sn, o = orc.gdn_step(q, k, v, np.zeros(S.shape[:2]), beta, S)
+    want = beta[..., None, None] * v[..., :, None] * k[..., None, :]
+    assert np.allclose(Sn, want, rtol=1e-14, atol=1e-15)
+    kq = np.einsum("shj,shj->sh", k, q)
+    assert np.allclose(o, beta[..., None] * v * kq[..., None], rtol=1e-12, atol=1e-13)
+
+
+def pin_gdn_matrix_form(orc):
+    """The closed matrix form of the gated delta rule,
+    S_new = alpha S (I - beta k k^T) + beta v k^T, evaluated with numpy
+    matrix products (a different evaluation order)."""
+    rng = np.random.default_rng(14)
+    S, q, k, v = _gdn_inputs(rng, n_seq=2, n_heads=4, d_k=16, d_v=12)
+    alpha = rng.uniform(0.5, 1.0, S.shape[:2])
+    beta = rng.uniform(0.0, 1.0, S.shape[:2])
+    Sn, o = orc.gdn_step(q, k, v, alpha, beta, S)
+    eye = np.eye(S.shape[3])
+    for s_ in range(S.shape[0]):
+        for h in range(S.shape[1]):
+            kk = np.outer(k[s_, h], k[s_, h])
+            want = alpha[s_, h] * S[s_, h] @ (eye - beta[s_, h] * kk) + beta[s_, h] * np.outer(v[s_, h], k[s_, h])
+            assert np.allclose(Sn[s_, h], want, rtol=1e-12, atol=1e-12)
+            assert np.allclose(o[s_, h], want @ q[s_, h], rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

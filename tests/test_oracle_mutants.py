@@ -37,6 +37,13 @@ MUTANTS = [
     # bytes, so the rounding itself is never exercised; the total is)
     ("record_total_short", "L.total = L.down_sb + up256(ds);", "L.total = L.down_sb;"),
     ("sb_section_swapped", "L.up_sb = L.gate_sb + up256(gs);", "L.up_sb = L.gate_sb;"),
+    ("gdn_no_decay", "for (size_t i = 0; i < (size_t)d_v * d_k; ++i) S[i] *= a;", ""),
+    ("gdn_delta_sign", "const double c = b * (vh[i] - u);", "const double c = b * (u - vh[i]);"),
+    ("gdn_no_delta", "const double c = b * (vh[i] - u);", "const double c = b * vh[i];"),
+    ("gdn_key_for_query", "for (int j = 0; j < d_k; ++j) o += row[j] * qh[j];",
+     "for (int j = 0; j < d_k; ++j) o += row[j] * kh[j];"),
+    ("gdn_transposed_gemv", "for (int j = 0; j < d_k; ++j) u += row[j] * kh[j];",
+     "for (int j = 0; j < d_k && j < d_v; ++j) u += S[(size_t)j * d_k + i] * kh[j];"),
 ]
 
 
