@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = [os.path.join(CSRC, "moe_kernels.hip"), os.path.join(CSRC, "moe_util.hip"),
-           os.path.join(CSRC, "moe_api.cpp")]
+           os.path.join(CSRC, "moe_gdn.hip"), os.path.join(CSRC, "moe_api.cpp")]
 HEADERS = [os.path.join(CSRC, "moe_internal.h"),
            os.path.join(os.path.dirname(HERE), "include", "moe.h")]
 

@@ -757,6 +757,35 @@ int moe_graph_destroy(moe_graph_t g) {
   return MOE_OK;
 }
 
+int moe_gdn_step(int n_seq, int n_heads, int d_k, int d_v, const float *q, const float *k,
+                 const float *v, const float *alpha, const float *beta, float *state,
+                 float *out, void *stream) {
+  if (n_seq < 1 || n_heads < 1) return fail(MOE_EINVAL, "n_seq = %d, n_heads = %d: need >= 1", n_seq, n_heads);
+  if ((long long)n_seq * n_heads > (1 << 24)) return fail(MOE_EINVAL, "n_seq * n_heads too large");
+  if (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128 && d_k != 256)
+    return fail(MOE_EUNSUPPORTED, "d_k = %d: only 16, 32, 64, 128 and 256 are built", d_k);
+  if (d_v < 1 || d_v > kMaxDim) return fail(MOE_EINVAL, "d_v = %d: need 1..%d", d_v, kMaxDim);
+  if (!q || !k || !v || !alpha || !beta || !state || !out) return fail(MOE_EINVAL, "a pointer is NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state, 16))
+    return fail(MOE_EALIGN, "q, k and state must be 16-byte aligned");
+  if (!aligned(v, 4) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(out, 4))
+    return fail(MOE_EALIGN, "v, alpha, beta and out must be 4-byte aligned");
+  GdnParams p;
+  p.n_sh = n_seq * n_heads;
+  p.d_k = d_k;
+  p.d_v = d_v;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.state = state;
+  p.out = out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_OTHER, [&] { return launch_gdn_step(p, s); }), "delta-rule step launch");
+  return MOE_OK;
+}
+
 int moe_fill_experts(void *dst, size_t stride, int n, uint64_t seed, int layer, int first_expert,
                      int hidden, int inter, int bits, double scale_lo, double scale_hi,
                      double bias_lo, double bias_hi, void *stream) {

@@ -237,6 +237,18 @@ extern thread_local LaunchEvents g_launch_events;
       hipLaunchKernelGGL(kern, grid, block, lds, stream, __VA_ARGS__);                       \
   } while (0)
 
+// gated delta-rule decode step (moe_gdn.hip)
+struct GdnParams {
+  int n_sh;                       // sequences * heads
+  int d_k, d_v;                   // d_k in {16, 32, 64, 128, 256}
+  const float *q, *k;             // [n_sh][d_k]
+  const float *v;                 // [n_sh][d_v]
+  const float *alpha, *beta;      // [n_sh]
+  float *state;                   // [n_sh][d_v][d_k], updated in place
+  float *out;                     // [n_sh][d_v]
+};
+hipError_t launch_gdn_step(const GdnParams &p, hipStream_t s);
+
 // bytes of the staged-x buffers for a row of `cols` columns at `bits`
 size_t xstage_pair_bytes(int cols, int bits);
 size_t xstage_sum_bytes(int cols, int bits);

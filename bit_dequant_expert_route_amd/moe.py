@@ -77,6 +77,7 @@ def _load():
         "moe_fill_experts": (I, [P, Z, I, C.c_uint64, I, I, I, I, I, C.c_double, C.c_double,
                                  C.c_double, C.c_double, P]),
         "moe_zero": (I, [P, Z, P]),
+        "moe_gdn_step": (I, [I, I, I, I, P, P, P, P, P, P, P, P]),
         "moe_profile_begin": (I, [I]),
         "moe_profile_end": (I, [C.POINTER(C.c_float), C.POINTER(C.c_int), I, C.POINTER(C.c_int)]),
     }
@@ -308,6 +309,15 @@ def profile_end(capacity: int):
     n = C.c_int(0)
     _check(_lib.moe_profile_end(ms, ids, capacity, C.byref(n)), "moe_profile_end")
     return [(KERNEL_NAMES.get(ids[i], str(ids[i])), float(ms[i])) for i in range(n.value)]
+
+
+def gdn_step(q, k, v, alpha, beta, state, out, stream=None):
+    """One gated delta-rule decode step (moe_gdn_step): state
+    [n_seq][n_heads][d_v][d_k] is updated in place, out [n_seq][n_heads][d_v]
+    receives S q.  fp32 device tensors."""
+    n_seq, n_heads, d_v, d_k = state.shape
+    _check(_lib.moe_gdn_step(n_seq, n_heads, d_k, d_v, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                             _ptr(beta), _ptr(state), _ptr(out), _stream(stream)), "moe_gdn_step")
 
 
 def zero(t, stream=None):

@@ -50,6 +50,7 @@ SEC_GATE_SB, SEC_UP_SB, SEC_DOWN_SB = 3, 4, 5
 # normal-draw stream ids
 STREAM_ROUTER, STREAM_GATEVEC, STREAM_X, STREAM_HRES, STREAM_UPDATE, STREAM_H0 = 1, 2, 3, 4, 5, 6
 STREAM_TOKEN_BASE, STREAM_TOKEN = 7, 8
+STREAM_GDN = 9
 
 GROUP = 64
 
@@ -360,3 +361,25 @@ def batch_residuals(cfg: LayerConfig, seed: int, rho: float, attempt: int = 0) -
     z0 = normals((cfg.hidden,), 1.0, seed, STREAM_TOKEN_BASE, attempt)
     zt = normals((cfg.n_tokens, cfg.hidden), 1.0, seed, STREAM_TOKEN, attempt)
     return (np.sqrt(rho) * z0[None, :] + np.sqrt(1.0 - rho) * zt).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# linear-attention decode step inputs
+# ----------------------------------------------------------------------------
+def gdn_inputs(seed: int, n_seq: int, n_heads: int, d_k: int, d_v: int, step: int = 0):
+    """fp32 inputs of one gated delta-rule step: q and k of unit length (the
+    model normalises them before the recurrence), v ~ N(0,1), decay alpha in
+    [0.9, 1), write strength beta in [0, 1), state ~ N(0, 0.1^2) (step 0
+    only; later steps carry the state)."""
+    shape = (n_seq, n_heads)
+    q = normals(shape + (d_k,), 1.0, seed, STREAM_GDN, 0, step)
+    k = normals(shape + (d_k,), 1.0, seed, STREAM_GDN, 1, step)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = normals(shape + (d_v,), 1.0, seed, STREAM_GDN, 2, step)
+    u = np.random.Generator(np.random.PCG64([seed, STREAM_GDN, 3, step])).random((2,) + shape)
+    alpha = 0.9 + 0.1 * u[0]
+    beta = u[1]
+    state = normals(shape + (d_v, d_k), 0.1, seed, STREAM_GDN, 4)
+    f = lambda a: np.ascontiguousarray(a, dtype=np.float32)  # noqa: E731
+    return f(q), f(k), f(v), f(alpha), f(beta), f(state)

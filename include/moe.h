@@ -245,6 +245,24 @@ int moe_profile_begin(int max_launches);
 int moe_profile_end(float *ms, int *kernel_ids, int capacity, int *n_out);
 
 /* ---------------------------------------------------------------------- */
+/* linear-attention decode step                                             */
+/* ---------------------------------------------------------------------- */
+/* One gated delta-rule step for every (sequence, head) pair: the state of
+ * the linear-attention layers, 64 heads of 128x128 on the pages, updated by a
+ * scale, a matrix-vector product and a rank-1 update ([openclawradar]
+ * "Accelerate BLAS for linear attention"; [a2a-fr] "Technical deep dive / 4").
+ * With S the d_v x d_k state of one head (row-major), in this order:
+ *     S <- alpha S;  u = S k;  S <- S + beta (v - u) k^T;  out = S q.
+ * q, k: [n_seq][n_heads][d_k]; v, out: [n_seq][n_heads][d_v];
+ * alpha, beta: [n_seq][n_heads]; state: [n_seq][n_heads][d_v][d_k] fp32,
+ * updated in place.  All device pointers, fp32.  d_k must be 16, 32, 64,
+ * 128 or 256 (MOE_EUNSUPPORTED otherwise), 1 <= d_v <= 8192; q, k and state
+ * 16-byte aligned (MOE_EALIGN).  state may not overlap the other arrays. */
+int moe_gdn_step(int n_seq, int n_heads, int d_k, int d_v, const float *q, const float *k,
+                 const float *v, const float *alpha, const float *beta, float *state,
+                 float *out, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* synthetic weights                                                        */
 /* ---------------------------------------------------------------------- */
 /* Fill n expert records at dst (stride bytes apart) with seeded synthetic

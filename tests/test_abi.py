@@ -123,3 +123,17 @@ def test_other_entry_points_validate():
     assert moe.lib.moe_zero(None, 16, None) == moe.MOE_EINVAL
     v = moe.WsView()
     assert moe.lib.moe_layer_ws_view(C.byref(L), 1, 0x400000, 16, C.byref(v)) == moe.MOE_EWORKSPACE
+
+
+def test_gdn_step_validates():
+    g = moe.lib.moe_gdn_step
+    ok = (0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000)
+    assert g(0, 64, 128, 128, *ok, None) == moe.MOE_EINVAL
+    assert g(1, 0, 128, 128, *ok, None) == moe.MOE_EINVAL
+    assert g(1, 64, 96, 128, *ok, None) == moe.MOE_EUNSUPPORTED
+    assert "d_k" in _err()
+    assert g(1, 64, 128, 0, *ok, None) == moe.MOE_EINVAL
+    assert g(1, 64, 128, 128, None, *ok[1:], None) == moe.MOE_EINVAL
+    assert g(1, 64, 128, 128, 0x1004, *ok[1:], None) == moe.MOE_EALIGN
+    assert g(1, 64, 128, 128, *ok[:5], 0x6008, 0x7000, None) == moe.MOE_EALIGN
+    assert g(1, 64, 128, 128, *ok[:6], 0x7002, None) == moe.MOE_EALIGN
