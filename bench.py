@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--instances", type=int, default=128)
     ap.add_argument("--workload", default="q4_layer",
-                    choices=["q4_layer", "q2_layer", "q4_stack", "q4_batch16"])
+                    choices=["q4_layer", "q2_layer", "q4_stack", "q4_batch16", "gdn_step"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-passes", type=int, default=3)
@@ -279,6 +279,59 @@ def bench_batch(cfg, args):
     return ms, rec, dict(instances=R, distinct=float(np.mean(distinct)))
 
 
+GDN_LAYERS, GDN_HEADS, GDN_DK, GDN_DV = 45, 64, 128, 128
+
+
+def bench_gdn(args):
+    """The linear-attention decode step of every linear-attention layer (45,
+    each with its own 64 x 128 x 128 fp32 state, 4 MiB) captured in one graph
+    and replayed; returns (ms per layer step, live per-kernel records)."""
+    import torch
+    from bit_dequant_expert_route_amd import moe
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4500)
+    L, Hh, dk, dv = GDN_LAYERS, GDN_HEADS, GDN_DK, GDN_DV
+    states = [torch.randn(1, Hh, dv, dk, generator=g, device="cuda") * 0.1 for _ in range(L)]
+    def unit(t):
+        return (t / t.norm(dim=-1, keepdim=True)).contiguous()
+    qs = [unit(torch.randn(1, Hh, dk, generator=g, device="cuda")) for _ in range(L)]
+    ks = [unit(torch.randn(1, Hh, dk, generator=g, device="cuda")) for _ in range(L)]
+    vs = [torch.randn(1, Hh, dv, generator=g, device="cuda") for _ in range(L)]
+    al = [0.9 + 0.1 * torch.rand(1, Hh, generator=g, device="cuda") for _ in range(L)]
+    be = [torch.rand(1, Hh, generator=g, device="cuda") for _ in range(L)]
+    outs = [torch.empty(1, Hh, dv, device="cuda") for _ in range(L)]
+
+    def one_pass(stream=None):
+        for i in range(L):
+            moe.gdn_step(qs[i], ks[i], vs[i], al[i], be[i], states[i], outs[i], stream=stream)
+
+    one_pass()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        moe.capture_begin(s)
+        one_pass(s)
+        graph = moe.capture_end(s, keep=(states, qs, ks, vs, al, be, outs))
+    for _ in range(args.warmup):
+        graph.launch(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(args.steps):
+        graph.launch(s)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps / L
+    assert all(bool(torch.isfinite(t).all()) for t in states)
+    n_launch = args.profile_passes * L
+    moe.profile_begin(n_launch)
+    for _ in range(args.profile_passes):
+        one_pass()
+    rec = moe.profile_end(n_launch)
+    graph.destroy()
+    return ms, rec
+
+
 def bench_layer(cfg, args):
     """Rotation set of R single-token layer decodes captured in one graph;
     returns (ms per layer, per-kernel live records, extras)."""
@@ -339,6 +392,33 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": a.numel(), "dispatches": 3}))
+        return
+
+    if args.workload == "gdn_step":
+        ms, rec = bench_gdn(args)
+        us = ms * 1000.0
+        state = GDN_HEADS * GDN_DV * GDN_DK * 4
+        step_bytes = 2 * state + GDN_HEADS * (2 * GDN_DK + 2 * GDN_DV + 2) * 4
+        kern = float(np.mean([m for _, m in rec]) * 1000.0)
+        achieved = step_bytes / (kern * 1e-6) / 1e9
+        line = {
+            "metric": "linear-attention (gated delta rule) decode step latency per layer",
+            "value": round(us, 3), "unit": "us", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms * GDN_LAYERS, 4),
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": f"gdn_step: {GDN_LAYERS} layers x {GDN_HEADS} heads x "
+                                   f"{GDN_DV}x{GDN_DK} fp32 state, one token (value = graph time / "
+                                   f"{GDN_LAYERS})", "hbm_bytes_per_unit": step_bytes},
+            "effective_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100.0 * step_bytes / (us * 1e-6) / 1e9 / PEAK_GBPS, 2),
+            "kernels_us": {"gdn_step": round(kern, 3)},
+            "roofline": {"bound": "hbm", "kernel": "k_gdn_step", "achieved": round(achieved, 1),
+                         "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+                         "traffic": None, "bytes_per_launch": step_bytes},
+            "cpu_baseline": None,
+        }
+        print(json.dumps(line), flush=True)
         return
 
     cfg = synth.CONFIGS[args.workload]
