@@ -53,9 +53,7 @@ __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_rea
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 __host__ __device__ __forceinline__ int ceil_log2(int v) {
-  int l = 0;
-  while ((1 << l) < v) ++l;
-  return l;
+  return v <= 1 ? 0 : 32 - __builtin_clz((unsigned)(v - 1));
 }
 
 template <int CTRL>
@@ -265,32 +263,6 @@ __device__ __forceinline__ void chunk_dot2(const uint4 &qa, const uint4 &qb,
   }
   da = a;
   db = b;
-}
-
-// load the x values of one chunk (columns col0 .. col0 + kCols - 1) as fp32
-template <int BITS, int XS>
-__device__ __forceinline__ void load_x_chunk(const void *x, const float *xl, int col0,
-                                             float (&v)[ChunkGeom<BITS>::kCols]) {
-  constexpr int NC = ChunkGeom<BITS>::kCols;
-  if constexpr (XS == XS_BF16) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + col0);
-#pragma unroll
-    for (int i = 0; i < NC / 8; ++i) {
-      const uint4 u = p[i];
-      v[8 * i + 0] = bf_lo(u.x); v[8 * i + 1] = bf_hi(u.x);
-      v[8 * i + 2] = bf_lo(u.y); v[8 * i + 3] = bf_hi(u.y);
-      v[8 * i + 4] = bf_lo(u.z); v[8 * i + 5] = bf_hi(u.z);
-      v[8 * i + 6] = bf_lo(u.w); v[8 * i + 7] = bf_hi(u.w);
-    }
-  } else {
-    const float *src = (XS == XS_F32) ? static_cast<const float *>(x) : xl;
-    const float4 *p = reinterpret_cast<const float4 *>(src + col0);
-#pragma unroll
-    for (int i = 0; i < NC / 4; ++i) {
-      const float4 u = p[i];
-      v[4 * i + 0] = u.x; v[4 * i + 1] = u.y; v[4 * i + 2] = u.z; v[4 * i + 3] = u.w;
-    }
-  }
 }
 
 // raw x of one chunk as loaded (bf16 words or fp32), before the staging math;
