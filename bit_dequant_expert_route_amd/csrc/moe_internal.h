@@ -23,7 +23,8 @@ enum XSrc : int {
   XS_F32 = 1,    // fp32 [H] in global memory
   XS_NORM = 2,   // x = rmsnorm(h + u), computed per workgroup into LDS
   XS_LDSPAD = 3, // fp32 in LDS, each code chunk's columns followed by kLdsPad
-                 // unused floats (spreads the lanes' 16-byte reads over banks)
+                 // floats, the first holding the chunk's column sum (the pad
+                 // spreads the lanes' 16-byte reads over banks)
 };
 constexpr int kLdsPad = 4;
 
