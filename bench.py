@@ -76,7 +76,7 @@ def kernel_bytes(cfg):
 
 def source_sha():
     h = hashlib.sha256()
-    for f in ("moe_kernels.hip", "moe_api.cpp", "moe_internal.h"):
+    for f in ("moe_kernels.hip", "moe_device.h", "moe_api.cpp", "moe_internal.h"):
         h.update(open(os.path.join(ROOT, "bit_dequant_expert_route_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
