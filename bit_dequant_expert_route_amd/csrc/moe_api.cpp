@@ -15,6 +15,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -80,7 +81,7 @@ bool dim_ok(int d) { return d >= 64 && d <= kMaxDim && d % kGroup == 0; }
 // ---------------------------------------------------------------------------
 struct WsLayout {
   size_t logits, sigma, h_routed, h_shared, y_shared, x_stage, hres_stage, xs_pairs, xs_sums,
-      h_pong, y_routed, g_count, g_expert, g_start, g_pair, total;
+      h_pong, y_routed, g_count, g_expert, g_start, g_pair, ids, total;
   size_t xs_pair_stride, xs_sum_stride;  // per token, in u32 / floats
 };
 
@@ -110,6 +111,7 @@ WsLayout ws_layout(const moe_layer_t *L, int T, int n_layers) {
   w.g_expert = o; o += batch ? up256(4 * (P + 1)) : 0;
   w.g_start = o; o += batch ? up256(4 * (P + 2)) : 0;
   w.g_pair = o; o += batch ? up256(4 * P) : 0;
+  w.ids = o; o += up256(4 * (size_t)kMaxK);  // cache slots of the routed experts (tier path)
   w.total = o;
   return w;
 }
@@ -697,6 +699,234 @@ int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *up
   }
   if (cur != h)
     MOE_TRY_HIP(timed(s, MOE_KERNEL_OTHER, [&] { return launch_copy_f32(h, cur, L->hidden, s); }), "copy launch");
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// host-memory expert tier
+// ---------------------------------------------------------------------------
+struct moe_tier_s {
+  const uint8_t *host;
+  int E;
+  size_t stride;
+  uint8_t *cache;
+  int n_slots;
+  std::vector<int32_t> slot_of;  // expert -> slot, or -1
+  std::vector<int32_t> owner;    // slot -> expert, or -1
+  std::vector<uint64_t> used;    // slot -> tick of its last use (0: never)
+  uint64_t tick = 0, hits = 0, misses = 0, bytes = 0;
+  int32_t *pinned = nullptr;     // page-locked: [kMaxK] routed ids, [kMaxK] their slots
+  std::mutex mu;
+};
+
+int moe_tier_create(const void *host_records, int n_experts, size_t expert_stride, void *cache,
+                    int n_slots, moe_tier_t *out) {
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  if (!host_records || !cache) return fail(MOE_EINVAL, "host_records / cache is NULL");
+  if (n_experts < 1 || n_experts > kMaxE) return fail(MOE_EINVAL, "n_experts = %d: need 1..1024", n_experts);
+  if (n_slots < kMaxK || n_slots > n_experts)
+    return fail(MOE_EINVAL, "n_slots = %d: need 8..n_experts", n_slots);
+  if (expert_stride == 0 || expert_stride % 256 || !aligned(cache, 256))
+    return fail(MOE_EALIGN, "cache and expert_stride must be 256-byte aligned");
+  moe_tier_s *t = new moe_tier_s;
+  t->host = static_cast<const uint8_t *>(host_records);
+  t->E = n_experts;
+  t->stride = expert_stride;
+  t->cache = static_cast<uint8_t *>(cache);
+  t->n_slots = n_slots;
+  t->slot_of.assign(n_experts, -1);
+  t->owner.assign(n_slots, -1);
+  t->used.assign(n_slots, 0);
+  *out = t;
+  return MOE_OK;
+}
+
+int moe_tier_destroy(moe_tier_t t) {
+  if (!t) return fail(MOE_EINVAL, "tier is NULL");
+  if (t->pinned) (void)hipHostFree(t->pinned);
+  delete t;
+  return MOE_OK;
+}
+
+int moe_tier_assign(moe_tier_t t, const int32_t *ids, int n, int32_t *slots, int32_t *miss) {
+  if (!t || !ids || !slots) return fail(MOE_EINVAL, "tier / ids / slots is NULL");
+  if (n < 0 || n > t->n_slots) return fail(MOE_EINVAL, "n = %d: need 0..n_slots", n);
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= t->E) return fail(MOE_EINVAL, "expert id %d out of range", ids[i]);
+  std::lock_guard<std::mutex> lk(t->mu);
+  const uint64_t now = ++t->tick;
+  for (int i = 0; i < n; ++i) {
+    const int e = ids[i];
+    int s = t->slot_of[e];
+    const bool hit = s >= 0;
+    if (hit) {
+      ++t->hits;
+    } else {
+      // least recently used slot not taken by this call (never-used slots
+      // have tick 0 and go first); n <= n_slots leaves one
+      s = -1;
+      for (int j = 0; j < t->n_slots; ++j)
+        if (t->used[j] < now && (s < 0 || t->used[j] < t->used[s])) s = j;
+      if (t->owner[s] >= 0) t->slot_of[t->owner[s]] = -1;
+      t->owner[s] = e;
+      t->slot_of[e] = s;
+      ++t->misses;
+    }
+    t->used[s] = now;
+    slots[i] = s;
+    if (miss) miss[i] = hit ? 0 : 1;
+  }
+  return MOE_OK;
+}
+
+int moe_tier_stats(moe_tier_t t, unsigned long long *hits, unsigned long long *misses,
+                   unsigned long long *bytes_copied) {
+  if (!t) return fail(MOE_EINVAL, "tier is NULL");
+  std::lock_guard<std::mutex> lk(t->mu);
+  if (hits) *hits = t->hits;
+  if (misses) *misses = t->misses;
+  if (bytes_copied) *bytes_copied = t->bytes;
+  return MOE_OK;
+}
+
+int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype, const void *x,
+                          const float *h_res, float *h_out, int32_t *topk_idx, float *topk_w,
+                          void *ws, size_t ws_bytes, void *stream) {
+  if (!L) return fail(MOE_EINVAL, "layer is NULL");
+  if (!t) return fail(MOE_EINVAL, "tier is NULL");
+  moe_layer_t Lc = *L;  // the routed records come from the tier's cache
+  Lc.experts = t->cache;
+  Lc.expert_stride = t->stride;
+  int st;
+  if ((st = check_layer(&Lc)) != MOE_OK) return st;
+  if (t->E != L->n_experts)
+    return fail(MOE_EINVAL, "the tier holds %d experts, the layer has %d", t->E, L->n_experts);
+  const size_t rb = moe_expert_bytes(L->hidden, L->inter, L->bits_routed, L->group);
+  if (t->stride < rb) return fail(MOE_EINVAL, "tier stride %zu < record size %zu", t->stride, rb);
+  if ((st = check_dtype(x_dtype, "x_dtype")) != MOE_OK) return st;
+  if ((st = check_vec(x, "x")) != MOE_OK) return st;
+  if ((st = check_vec(h_res, "h_res")) != MOE_OK) return st;
+  if ((st = check_vec(h_out, "h_out")) != MOE_OK) return st;
+  if (h_out == h_res) return fail(MOE_EINVAL, "h_out may not alias h_res");
+  if (!topk_idx || !topk_w) return fail(MOE_EINVAL, "topk_idx / topk_w is NULL");
+  if (!aligned(topk_idx, 4) || !aligned(topk_w, 4)) return fail(MOE_EALIGN, "topk outputs must be 4-byte aligned");
+  const WsLayout wl = ws_layout(L, 1, 0);
+  if ((st = check_ws(ws, ws_bytes, wl.total)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  MOE_TRY_HIP(hipStreamIsCapturing(s, &cs), "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(MOE_EINVAL, "the tier path waits for the routing on the host and cannot be captured");
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  float *logits = reinterpret_cast<float *>(wsb + wl.logits);
+  float *sigma = reinterpret_cast<float *>(wsb + wl.sigma);
+  float *h_routed = reinterpret_cast<float *>(wsb + wl.h_routed);
+  float *h_shared = reinterpret_cast<float *>(wsb + wl.h_shared);
+  float *y_shared = reinterpret_cast<float *>(wsb + wl.y_shared);
+  int32_t *slot_ids = reinterpret_cast<int32_t *>(wsb + wl.ids);
+  const int K = L->top_k;
+  const int xsrc = x_dtype == MOE_BF16 ? XS_BF16 : XS_F32;
+  const bool same = L->bits_shared == L->bits_routed;
+
+  // router rows, shared gate (and the shared gate/up at another width), top-K
+  HeadParams hp = head_params(&Lc, 1);
+  hp.xsrc = xsrc;
+  hp.x = x;
+  hp.logits = logits;
+  hp.sigma = sigma;
+  hp.h_shared = h_shared;
+  hp.n_shared_waves = same ? 0 : 1;
+  hp.bits_routed = L->bits_routed;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_HEAD, [&] { return launch_head(hp, s); }), "router launch");
+  TopkParams tp;
+  tp.logits = logits;
+  tp.T = 1;
+  tp.E = L->n_experts;
+  tp.K = K;
+  tp.renorm = L->renorm_topk;
+  tp.idx = topk_idx;
+  tp.w = topk_w;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_TOPK, [&] { return launch_topk(tp, s); }), "top-K launch");
+
+  // the routing on the host, then the missing records into their slots (the
+  // previous call's copies from the page-locked buffer ended at this wait)
+  if (!t->pinned) {  // first call: the page-locked routing buffer (host memory)
+    void *pin = nullptr;
+    MOE_TRY_HIP(hipHostMalloc(&pin, 2 * kMaxK * sizeof(int32_t), hipHostMallocDefault),
+                "hipHostMalloc (routing buffer)");
+    t->pinned = static_cast<int32_t *>(pin);
+  }
+  int32_t *ids = t->pinned, *slots = t->pinned + kMaxK;
+  int32_t miss[kMaxK];
+  MOE_TRY_HIP(hipMemcpyAsync(ids, topk_idx, K * sizeof(int32_t), hipMemcpyDeviceToHost, s), "routing copy");
+  MOE_TRY_HIP(hipStreamSynchronize(s), "waiting for the routing");
+  if ((st = moe_tier_assign(t, ids, K, slots, miss)) != MOE_OK) return st;
+  for (int k = 0; k < K; ++k) {
+    if (!miss[k]) continue;
+    MOE_TRY_HIP(hipMemcpyAsync(t->cache + (size_t)slots[k] * t->stride, t->host + (size_t)ids[k] * t->stride,
+                               rb, hipMemcpyHostToDevice, s),
+                "expert record copy");
+    std::lock_guard<std::mutex> lk(t->mu);
+    t->bytes += rb;
+  }
+  MOE_TRY_HIP(hipMemcpyAsync(slot_ids, slots, K * sizeof(int32_t), hipMemcpyHostToDevice, s), "slot copy");
+
+  // gate/up of the cached records (+ the shared expert), down + combine
+  GateUpParams gp;
+  memset(&gp, 0, sizeof gp);
+  gp.H = L->hidden;
+  gp.I = L->inter;
+  gp.E = t->n_slots;
+  gp.K = K;
+  gp.bits = L->bits_routed;
+  gp.experts = t->cache;
+  gp.stride = t->stride;
+  gp.shared_rec = static_cast<const uint8_t *>(L->shared_expert);
+  gp.shared_ok = same;
+  gp.off = offsets_of(L->hidden, L->inter, L->bits_routed);
+  gp.soff = offsets_of(L->hidden, L->inter, L->bits_shared);
+  gp.ids = slot_ids;
+  gp.n = K;
+  gp.xsrc = xsrc;
+  gp.x = x;
+  gp.h_out = h_routed;
+  gp.with_shared = same;
+  gp.h_shared_out = h_shared;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_GATEUP, [&] { return launch_gateup(gp, s); }), "gate/up launch");
+  DownParams dp;
+  memset(&dp, 0, sizeof dp);
+  dp.H = L->hidden;
+  dp.I = L->inter;
+  dp.E = t->n_slots;
+  dp.experts = t->cache;
+  dp.stride = t->stride;
+  dp.shared_rec = gp.shared_rec;
+  dp.off = gp.off;
+  dp.soff = gp.soff;
+  dp.shared_ok = 1;
+  if (!same) {
+    DownParams sp = dp;
+    sp.combine = 0;
+    sp.bits_r = L->bits_shared;
+    sp.ids = nullptr;
+    sp.n = 1;
+    sp.h = h_shared;
+    sp.y = y_shared;
+    MOE_TRY_HIP(timed(s, MOE_KERNEL_DOWN_Y, [&] { return launch_down(sp, s); }), "shared down launch");
+  }
+  dp.combine = 1;
+  dp.bits_r = L->bits_routed;
+  dp.bits_s = L->bits_shared;
+  dp.idx = slot_ids;
+  dp.w = topk_w;
+  dp.K = K;
+  dp.sigma = sigma;
+  dp.h_routed = h_routed;
+  dp.h_shared = same ? h_shared : nullptr;
+  dp.y = same ? nullptr : y_shared;
+  dp.h_res = h_res;
+  dp.out = h_out;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_DOWN, [&] { return launch_down(dp, s); }), "down/combine launch");
   return MOE_OK;
 }
 

@@ -78,6 +78,12 @@ def _load():
                                  C.c_double, C.c_double, P]),
         "moe_zero": (I, [P, Z, P]),
         "moe_gdn_step": (I, [I, I, I, I, P, P, P, P, P, P, P, P]),
+        "moe_tier_create": (I, [P, I, Z, P, I, C.POINTER(P)]),
+        "moe_tier_destroy": (I, [P]),
+        "moe_tier_assign": (I, [P, P, I, P, P]),
+        "moe_tier_layer_decode": (I, [C.POINTER(LayerStruct), P, I, P, P, P, P, P, P, Z, P]),
+        "moe_tier_stats": (I, [P, C.POINTER(C.c_ulonglong), C.POINTER(C.c_ulonglong),
+                               C.POINTER(C.c_ulonglong)]),
         "moe_profile_begin": (I, [I]),
         "moe_profile_end": (I, [C.POINTER(C.c_float), C.POINTER(C.c_int), I, C.POINTER(C.c_int)]),
     }
@@ -322,3 +328,48 @@ def gdn_step(q, k, v, alpha, beta, state, out, stream=None):
 
 def zero(t, stream=None):
     _check(_lib.moe_zero(_ptr(t), t.numel() * t.element_size(), _stream(stream)), "moe_zero")
+
+
+class Tier:
+    """Host-memory expert tier (moe_tier_*): `host` holds the layer's E routed
+    records (a page-locked CPU uint8 tensor, or any host address), `cache` is
+    a CUDA uint8 tensor of n_slots * stride bytes.  Both must outlive the
+    tier."""
+
+    def __init__(self, host, n_experts: int, stride: int, cache, n_slots: int, host_ptr: int | None = None):
+        self.host, self.cache = host, cache
+        hp = host_ptr if host_ptr is not None else host.data_ptr()
+        cp = cache if isinstance(cache, int) else _ptr(cache)
+        h = C.c_void_p()
+        _check(_lib.moe_tier_create(hp, n_experts, stride, cp, n_slots, C.byref(h)), "moe_tier_create")
+        self.h = h
+
+    def assign(self, ids):
+        n = len(ids)
+        a = (C.c_int32 * max(n, 1))(*ids)
+        sl = (C.c_int32 * max(n, 1))()
+        ms = (C.c_int32 * max(n, 1))()
+        _check(_lib.moe_tier_assign(self.h, a, n, sl, ms), "moe_tier_assign")
+        return list(sl)[:n], list(ms)[:n]
+
+    def stats(self):
+        h, m, b = C.c_ulonglong(), C.c_ulonglong(), C.c_ulonglong()
+        _check(_lib.moe_tier_stats(self.h, C.byref(h), C.byref(m), C.byref(b)), "moe_tier_stats")
+        return int(h.value), int(m.value), int(b.value)
+
+    def layer_decode(self, layer: "Layer", x, h_res, h_out, topk_idx, topk_w, ws=None, stream=None):
+        ws, wp, wb = _ws(layer, ws, 1)
+        _check(_lib.moe_tier_layer_decode(C.byref(layer.s), self.h, _dtype_code(x), _ptr(x), _ptr(h_res),
+                                          _ptr(h_out), _ptr(topk_idx), _ptr(topk_w), wp, wb,
+                                          _stream(stream)), "moe_tier_layer_decode")
+
+    def close(self):
+        if self.h:
+            _check(_lib.moe_tier_destroy(self.h), "moe_tier_destroy")
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

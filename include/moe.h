@@ -201,6 +201,45 @@ int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *up
                      void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* host-memory expert tier ([openclawradar] "SSD expert streaming" and      */
+/* [a2a-fr] "Technical deep dive": only the routed experts of a token are   */
+/* read, on demand, after the routing; the OS page cache serves repeats)    */
+/* ---------------------------------------------------------------------- */
+typedef struct moe_tier_s *moe_tier_t;
+/* A cache of n_slots routed-expert records in device memory in front of all
+ * E records of one layer in host memory.
+ *   host_records  E records, expert_stride bytes apart, caller-owned host
+ *                 memory (page-locked, e.g. hipHostMalloc, for the copies to
+ *                 be asynchronous)
+ *   cache         n_slots x expert_stride bytes of device memory,
+ *                 caller-owned, 256-byte aligned
+ * K <= 8 <= n_slots <= E <= 1024; expert_stride a multiple of 256.  Slots are
+ * replaced least recently used first.  The tier object is host bookkeeping
+ * (no device memory is allocated); one stream at a time may use a tier. */
+int moe_tier_create(const void *host_records, int n_experts, size_t expert_stride,
+                    void *cache, int n_slots, moe_tier_t *out);
+int moe_tier_destroy(moe_tier_t t);
+/* The slots of n expert ids (host arrays, 0 <= n <= n_slots): slots[i] holds
+ * expert ids[i] after the call, miss[i] (may be NULL) is 1 when it had to be
+ * brought in.  Bookkeeping only, no copy is issued; moe_tier_layer_decode
+ * calls it with the routing of each token. */
+int moe_tier_assign(moe_tier_t t, const int32_t *ids, int n, int32_t *slots, int32_t *miss);
+/* moe_layer_decode for one token with the routed experts read through the
+ * tier: router + top-K on the device, the K ids to the host (the call waits
+ * for them once, so it cannot be captured into a graph: MOE_EINVAL), the
+ * missing records copied into their slots (host to device, on `stream`), then
+ * gate/up and down + combine on the cached records.  L->experts and
+ * L->expert_stride are not used; the layer's router, gate vector and shared
+ * expert are.  The outputs (topk_idx holds expert ids, not slots) equal those
+ * of moe_layer_decode. */
+int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype, const void *x,
+                          const float *h_res, float *h_out, int32_t *topk_idx, float *topk_w,
+                          void *ws, size_t ws_bytes, void *stream);
+/* Hits, misses and record bytes copied so far (any pointer may be NULL). */
+int moe_tier_stats(moe_tier_t t, unsigned long long *hits, unsigned long long *misses,
+                   unsigned long long *bytes_copied);
+
+/* ---------------------------------------------------------------------- */
 /* HIP graphs ([openclawradar] "Deferred GPU expert compute": the expert     */
 /* pass is queued without a host wait)                                      */
 /* ---------------------------------------------------------------------- */
