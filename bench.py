@@ -364,13 +364,16 @@ def bench_layer(cfg, args):
     for _ in range(args.warmup):
         graph.launch(s)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(args.steps):
+    # an event between replays: the whole span gives the value, each replay
+    # its own latency (median, p90)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(s)
+    for k in range(args.steps):
         graph.launch(s)
-    e1.record(s)
+        ev[k + 1].record(s)
     torch.cuda.synchronize()
-    ms_layer = e0.elapsed_time(e1) / args.steps / R
+    ms_layer = ev[0].elapsed_time(ev[-1]) / args.steps / R
+    per = [ev[k].elapsed_time(ev[k + 1]) * 1000.0 / R for k in range(args.steps)]
     # per-kernel durations (events recorded by each dispatch, eager launches)
     n_launch = args.profile_passes * R * 4
     moe.profile_begin(n_launch)
@@ -378,7 +381,8 @@ def bench_layer(cfg, args):
         one_pass()
     rec = moe.profile_end(n_launch)
     graph.destroy()
-    return ms_layer, rec, {}
+    return ms_layer, rec, {"replay_us_per_layer_median": round(float(np.median(per)), 3),
+                           "replay_us_per_layer_p90": round(float(np.percentile(per, 90)), 3)}
 
 
 def bench_tier(cfg, args):
@@ -525,7 +529,7 @@ def main():
         ms_layer, rec, extra = bench_layer(cfg, args)
         us_per_layer = ms_layer * 1000.0
         ms_per_step = ms_layer * args.instances
-        unit_note = {"layer_instances_per_step": args.instances}
+        unit_note = {"layer_instances_per_step": args.instances, **extra}
         bytes_per_unit = kb["layer_total"]
 
     per = {}

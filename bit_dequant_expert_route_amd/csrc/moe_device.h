@@ -37,11 +37,6 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-
 // Sum over aligned groups of 2^lg lanes; every lane of a group gets the sum.
 __device__ __forceinline__ float seg_sum(float v, int lg) {
   if (lg >= 1) v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
