@@ -111,6 +111,7 @@ struct GroupedParams {
   float *y_shared;                // [T][H]
   int rows_per_wave, tiles;       // set by the launcher (tiles of four waves)
   int tok_batch;                  // tokens staged in LDS at a time (launcher)
+  int shared_split;               // token ranges of the shared expert's items (launcher)
 };
 hipError_t launch_gateup_grouped(const GroupedParams &p, hipStream_t s);
 hipError_t launch_down_grouped(const GroupedParams &p, hipStream_t s);

@@ -411,16 +411,33 @@ struct GroupRef {
   bool shared;
 };
 
-__device__ __forceinline__ GroupRef group_ref(const GroupedParams &p, int g, int U) {
+// Work items, in order: the shared expert's (its T tokens in shared_split
+// ranges, each range over every row tile: it holds the most work, so it
+// starts first and no item carries every token), then the row tiles of the
+// routed groups in expert order.  Returns the item's group and row tile.
+__device__ __forceinline__ int n_work_items(const GroupedParams &p, int U) {
+  return ((p.do_shared ? p.shared_split : 0) + U) * p.tiles;
+}
+
+__device__ __forceinline__ GroupRef item_ref(const GroupedParams &p, int item, int U, int &tile) {
   GroupRef r;
   const int lane = lane_id();
-  r.shared = p.do_shared && g == U;
-  if (r.shared) {
+  const int n_sh = p.do_shared ? p.shared_split * p.tiles : 0;
+  if (item < n_sh) {
+    const int part = item / p.tiles;
+    tile = item - part * p.tiles;
+    const int per = (p.T + p.shared_split - 1) / p.shared_split;
+    const int t0 = part * per;
+    r.shared = true;
     r.id = kSharedId;
-    r.n = p.T;
-    r.pair = lane;
-    r.tok = lane;
+    r.n = p.T - t0 < per ? p.T - t0 : per;
+    r.pair = t0 + lane;
+    r.tok = t0 + lane;
   } else {
+    const int q = item - n_sh;
+    const int g = q / p.tiles;
+    tile = q - g * p.tiles;
+    r.shared = false;
     r.id = wave_uniform(p.g_expert[g]);
     const int s0 = wave_uniform(p.g_start[g]);
     r.n = wave_uniform(p.g_start[g + 1]) - s0;
@@ -511,7 +528,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedParams p) {
   constexpr int CS = lds_chunk_words<Stage>();
   const int wv = wave_uniform(threadIdx.x >> 6);
   const int U = p.do_routed ? wave_uniform(p.g_count[0]) : 0;
-  const int n_items = (U + (p.do_shared ? 1 : 0)) * p.tiles;
+  const int n_items = n_work_items(p, U);
   const RowMap m = row_map<BITS>(p.H);
   const int cpr = m.cpr;
   // the next item's weight rows are requested before this item's tokens are
@@ -520,9 +537,9 @@ __global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedParams p) {
   GroupRef ngr;
   int nrow0 = 0;
   auto fetch = [&](int item, GUTile<BITS, NCH, NPASS> &t, GroupRef &r, int &row0) {
-    const int g = item < n_items ? item / p.tiles : 0;
-    row0 = ((item - g * p.tiles) * 4 + wv) * p.rows_per_wave;
-    r = group_ref(p, g, U);
+    int tile;
+    r = item_ref(p, item < n_items ? item : 0, U, tile);
+    row0 = (tile * 4 + wv) * p.rows_per_wave;
     const bool v = r.shared ? true : (r.id >= 0 && r.id < p.E);
     const uint8_t *rec = r.shared ? p.shared_rec : p.experts + (size_t)(v ? r.id : 0) * p.stride;
     gu_load(t, rec, r.shared ? p.soff : p.off, m, p.I, row0);
@@ -572,16 +589,16 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedParams p) {
   constexpr int PC = NC + kLdsPad;
   const int wv = wave_uniform(threadIdx.x >> 6);
   const int U = p.do_routed ? wave_uniform(p.g_count[0]) : 0;
-  const int n_items = (U + (p.do_shared ? 1 : 0)) * p.tiles;
+  const int n_items = n_work_items(p, U);
   const RowMap m = row_map<BITS>(p.I);
   const int tok_floats = (p.I / NC) * PC;
   DnTile<BITS, NCH, NPASS> next;
   GroupRef ngr;
   int nrow0 = 0;
   auto fetch = [&](int item, DnTile<BITS, NCH, NPASS> &t, GroupRef &r, int &row0) {
-    const int g = item < n_items ? item / p.tiles : 0;
-    row0 = ((item - g * p.tiles) * 4 + wv) * p.rows_per_wave;
-    r = group_ref(p, g, U);
+    int tile;
+    r = item_ref(p, item < n_items ? item : 0, U, tile);
+    row0 = (tile * 4 + wv) * p.rows_per_wave;
     const bool v = r.shared ? true : (r.id >= 0 && r.id < p.E);
     const uint8_t *rec = r.shared ? p.shared_rec : p.experts + (size_t)(v ? r.id : 0) * p.stride;
     down_load(t, rec, r.shared ? p.soff : p.off, p.H, m, row0);
@@ -818,9 +835,15 @@ hipError_t launch_route_group(const RouteGroupParams &p, hipStream_t s) {
 
 static constexpr size_t kGroupedLds = 48 * 1024;
 
+// the shared expert's tokens in at most four ranges
+static void set_shared_split(GroupedParams &p) {
+  const int per = (p.T + 3) / 4;
+  p.shared_split = (p.T + per - 1) / per;
+}
+
 static dim3 grouped_grid(const GroupedParams &p, long cap) {
-  const int max_groups = (p.T * p.K < p.E ? p.T * p.K : p.E) + 1;
-  long blocks = (long)max_groups * p.tiles;
+  const int routed = p.do_routed ? (p.T * p.K < p.E ? p.T * p.K : p.E) : 0;
+  long blocks = (long)(routed + (p.do_shared ? p.shared_split : 0)) * p.tiles;
   if (blocks > cap) blocks = cap;
   return dim3((unsigned)(blocks < 1 ? 1 : blocks));
 }
@@ -841,6 +864,7 @@ hipError_t launch_gateup_grouped(const GroupedParams &p0, hipStream_t s) {
   if (nch >= 2 && npass > 2) npass = 2;
   p.rows_per_wave = npass * rpp;
   p.tiles = (p.I + 4 * p.rows_per_wave - 1) / (4 * p.rows_per_wave);
+  set_shared_split(p);
   const dim3 grid = grouped_grid(p, 512);
   const int cpr = p.H * p.bits / 128;
 #define MOE_GG(BITS, XS)                                                                       \
@@ -867,6 +891,7 @@ hipError_t launch_down_grouped(const GroupedParams &p0, hipStream_t s) {
   const int npass = nch >= 4 ? 1 : (rpp >= 8 ? 1 : (rpp >= 4 ? 2 : 4));
   p.rows_per_wave = npass * rpp;
   p.tiles = (p.H + 4 * p.rows_per_wave - 1) / (4 * p.rows_per_wave);
+  set_shared_split(p);
   const dim3 grid = grouped_grid(p, 768);
   const int nc = 128 / p.bits;
   const size_t per_tok = (size_t)(p.I / nc) * (nc + kLdsPad) * 4;
