@@ -531,7 +531,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedParams p) {
   const int n_items = n_work_items(p, U);
   const RowMap m = row_map<BITS>(p.H);
   const int cpr = m.cpr;
-  // the next item's weight rows are requested before this item's tokens are
+  // the next item's weight rows are requested while this item's tokens are
   // worked through
   GUTile<BITS, NCH, NPASS> next;
   GroupRef ngr;
@@ -549,7 +549,6 @@ __global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedParams p) {
     const GUTile<BITS, NCH, NPASS> tile = next;
     const GroupRef gr = ngr;
     const int row0 = nrow0;
-    if (item + (int)gridDim.x < n_items) fetch(item + gridDim.x, next, ngr, nrow0);
     const bool valid = gr.shared ? true : (gr.id >= 0 && gr.id < p.E);
     for (int i0 = 0; i0 < gr.n; i0 += p.tok_batch) {
       const int nb = gr.n - i0 < p.tok_batch ? gr.n - i0 : p.tok_batch;
@@ -564,6 +563,10 @@ __global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedParams p) {
           lds_store<BITS>(lds_x + (size_t)(b * cpr + c) * CS, group_stage_chunk<BITS, XS>(p, tok, c));
       }
       __syncthreads();
+      // the next item's weight rows are requested once this item's first
+      // activations are staged: loads complete in order, so requested
+      // earlier they would hold up the staging
+      if (i0 == 0 && item + (int)gridDim.x < n_items) fetch(item + gridDim.x, next, ngr, nrow0);
       for (int b = 0; b < nb; ++b) {
         Stage xs[NCH];
 #pragma unroll
@@ -608,7 +611,6 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedParams p) {
     const DnTile<BITS, NCH, NPASS> tile = next;
     const GroupRef gr = ngr;
     const int row0 = nrow0;
-    if (item + (int)gridDim.x < n_items) fetch(item + gridDim.x, next, ngr, nrow0);
     const bool valid = gr.shared ? true : (gr.id >= 0 && gr.id < p.E);
     for (int i0 = 0; i0 < gr.n; i0 += p.tok_batch) {
       const int nb = gr.n - i0 < p.tok_batch ? gr.n - i0 : p.tok_batch;
@@ -621,6 +623,9 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedParams p) {
           lds_put_chunk4<BITS>(lds_h + b * tok_floats, col, *reinterpret_cast<const float4 *>(hin + col));
       }
       __syncthreads();
+      // the next item's rows are requested once this item's first inputs are
+      // staged (loads complete in order)
+      if (i0 == 0 && item + (int)gridDim.x < n_items) fetch(item + gridDim.x, next, ngr, nrow0);
       for (int b = 0; b < nb; ++b) {
         const int pair = __builtin_amdgcn_readlane(gr.pair, i0 + b);
         const int tok = __builtin_amdgcn_readlane(gr.tok, i0 + b);
