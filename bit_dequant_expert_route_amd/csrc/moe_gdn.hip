@@ -6,26 +6,13 @@
 //     S <- alpha S;  u = S k;  S <- S + beta (v - u) k^T;  o = S q.
 // Row i of the result depends on row i of S only, so one pass reads and
 // writes each row once: the step is bound by the state's HBM traffic.
-#include "moe_internal.h"
+#include "moe_device.h"
 
 #include <stdint.h>
 
 namespace moe_impl {
 
 namespace {
-
-__device__ __forceinline__ int gdn_lane() { return threadIdx.x & 63; }
-
-// sum over aligned groups of 2^lg lanes (every lane of a group gets it)
-__device__ __forceinline__ float gdn_seg_sum(float v, int lg) {
-  if (lg >= 1) v += __shfl_xor(v, 1, 64);
-  if (lg >= 2) v += __shfl_xor(v, 2, 64);
-  if (lg >= 3) v += __shfl_xor(v, 4, 64);
-  if (lg >= 4) v += __shfl_xor(v, 8, 64);
-  if (lg >= 5) v += __shfl_xor(v, 16, 64);
-  if (lg >= 6) v += __shfl_xor(v, 32, 64);
-  return v;
-}
 
 __device__ __forceinline__ float dot4(const float4 &a, const float4 &b) {
   return fmaf(a.w, b.w, fmaf(a.z, b.z, fmaf(a.y, b.y, a.x * b.x)));
@@ -40,7 +27,7 @@ constexpr int kGdnPasses = 2;
 
 __global__ __launch_bounds__(kBlock) void k_gdn_step(GdnParams p) {
   const int wave = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-  const int lane = gdn_lane();
+  const int lane = lane_id();
   const int lpr = p.d_k >> 2;              // lanes per row (power of two, <= 64)
   const int lg = 31 - __clz(lpr);
   const int li = lane & (lpr - 1), rip = lane >> lg;
@@ -71,13 +58,13 @@ __global__ __launch_bounds__(kBlock) void k_gdn_step(GdnParams p) {
     x.y *= a;
     x.z *= a;
     x.w *= a;
-    const float u = gdn_seg_sum(dot4(x, k4), lg);  // u_r = (alpha S k)_r
+    const float u = seg_sum(dot4(x, k4), lg);  // u_r = (alpha S k)_r
     const float c = b * (vi[ps] - u);
     x.x = fmaf(c, k4.x, x.x);                       // rank-1 delta update
     x.y = fmaf(c, k4.y, x.y);
     x.z = fmaf(c, k4.z, x.z);
     x.w = fmaf(c, k4.w, x.w);
-    const float o = gdn_seg_sum(dot4(x, q4), lg);  // o_r = (S_new q)_r
+    const float o = seg_sum(dot4(x, q4), lg);  // o_r = (S_new q)_r
     if (r < p.d_v) {
       reinterpret_cast<float4 *>(S + (size_t)r * p.d_k)[li] = x;
       if (li == 0) p.out[(size_t)sh * p.d_v + r] = o;
