@@ -21,9 +21,11 @@ __device__ __forceinline__ float dot4(const float4 &a, const float4 &b) {
 }  // namespace
 
 // A row of d_k values is held by d_k / 4 lanes (16 bytes each); a wave takes
-// 64 / (d_k / 4) rows per pass and kGdnPasses passes.  Loads of all passes
-// are issued before the arithmetic.
-constexpr int kGdnPasses = 2;
+// 64 / (d_k / 4) rows per pass and kGdnPasses passes (loads of all passes
+// before the arithmetic).  One pass, the most waves, measured fastest for
+// 64 heads of 128 x 128 (3.6 us per step against 4.0 for two passes and 4.3
+// for four).
+constexpr int kGdnPasses = 1;
 
 __global__ __launch_bounds__(kBlock) void k_gdn_step(GdnParams p) {
   const int wave = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
