@@ -97,3 +97,18 @@ def test_q4_stack_60_layers():
     if free < need:
         pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory, {free / 2**30:.0f} GiB free")
     _run(cfg, 3, graph_replays=1)
+
+
+STACK_EDGE = {
+    # 2-bit experts throughout; a 2-bit layer with a 4-bit shared expert (the
+    # shared gate/up runs in the router kernel, its down in its own launch);
+    # rows that do not fill a wave
+    "q2": synth.LayerConfig("stack_q2", 256, 128, 16, 2, 2, 2, "bf16", "bf16", "f32", n_layers=6),
+    "mixed": synth.LayerConfig("stack_mixed", 256, 128, 16, 2, 2, 4, "f32", "f32", "f32", n_layers=6),
+    "ragged": synth.LayerConfig("stack_ragged", 192, 320, 16, 2, 4, 4, "bf16", "bf16", "f32", n_layers=6),
+}
+
+
+@pytest.mark.parametrize("name", list(STACK_EDGE))
+def test_stack_edges(name):
+    _run(STACK_EDGE[name], 13, graph_replays=1)
