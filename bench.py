@@ -455,6 +455,24 @@ def bench_tier(cfg, args):
     return dt * 1000.0 / N, rec, extra
 
 
+def read_peak_gbps():
+    """Streaming-read rate of this GPU: a 4 GiB sum (read-bound), best of 3."""
+    import torch
+    a = torch.ones(1 << 29, dtype=torch.float64, device="cuda")  # 4 GiB
+    a.sum()
+    best = 0.0
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        a.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, a.numel() * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del a
+    torch.cuda.empty_cache()
+    return best
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -500,6 +518,7 @@ def main():
         print(json.dumps(line), flush=True)
         return
 
+    read_gbps = read_peak_gbps()
     cfg = synth.CONFIGS["q4_layer" if args.workload == "q4_tier" else args.workload]
     kb = kernel_bytes(cfg)
     if args.workload == "q4_tier":
@@ -578,6 +597,8 @@ def main():
                    "hbm_bytes_per_unit": bytes_per_unit, **unit_note},
         "effective_GBps": round(bytes_per_unit / (us_per_layer * 1e-6) / 1e9, 1),
         "pct_hbm_peak": round(100.0 * bytes_per_unit / (us_per_layer * 1e-6) / 1e9 / PEAK_GBPS, 2),
+        "measured_read_peak_GBps": round(read_gbps, 1),
+        "pct_measured_read_peak": round(100.0 * bytes_per_unit / (us_per_layer * 1e-6) / 1e9 / read_gbps, 2),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
         "roofline": {"bound": "hbm", "kernel": dom_kernel,
                      "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
