@@ -130,37 +130,61 @@ def build_rotation(cfg, R, seed0=1000):
 
 def cpu_baseline(cfg, budget_s):
     """fp64 oracle on the host: route + K routed experts + shared + combine for
-    as many sampled layer instances as fit the time budget."""
+    as many sampled layer instances as fit the time budget, on all the
+    oracle's threads, then on one thread for a third of that budget."""
     import oracle
     from bit_dequant_expert_route_amd import synth
     orc = oracle.get()
     H, I = cfg.hidden, cfg.inter
-    times = []
-    t_end = time.perf_counter() + budget_s
-    i = 0
-    while time.perf_counter() < t_end or i == 0:
-        seed = 5000 + i
-        router = synth.router_weights(cfg, seed)
-        gate = synth.shared_gate_vector(cfg, seed)
-        h_res = synth.residual(cfg, seed)
-        x64 = orc.rmsnorm(h_res.astype(np.float64))
-        xb = synth.bf16_to_f32(synth.f64_to_bf16_rne(x64)).astype(np.float64)
-        # weight generation is excluded from the timed region
-        logits = orc.router(router, cfg.router_dtype, xb)
-        idx = orc.topk(logits, cfg.top_k)
-        recs = [synth.make_record(seed, 0, int(e), H, I, cfg.bits_routed) for e in idx]
-        shared = synth.make_record(seed, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared)
-        t0 = time.perf_counter()
-        r = orc.route(router, cfg.router_dtype, gate, cfg.gate_dtype, xb, cfg.top_k, True)
-        ys = [orc.expert(rec, H, I, cfg.bits_routed, xb)[1] for rec in recs]
-        ysh = orc.expert(shared, H, I, cfg.bits_shared, xb)[1]
-        orc.combine(h_res.astype(np.float64), np.stack(ys), r["w"], ysh, r["sigma"])
-        times.append(time.perf_counter() - t0)
-        i += 1
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def sample(budget, first):
+        times = []
+        t_end = time.perf_counter() + budget
+        i = 0
+        while time.perf_counter() < t_end or i == 0:
+            seed = first + i
+            router = synth.router_weights(cfg, seed)
+            gate = synth.shared_gate_vector(cfg, seed)
+            h_res = synth.residual(cfg, seed)
+            x64 = orc.rmsnorm(h_res.astype(np.float64))
+            xb = synth.bf16_to_f32(synth.f64_to_bf16_rne(x64)).astype(np.float64)
+            # weight generation is excluded from the timed region
+            logits = orc.router(router, cfg.router_dtype, xb)
+            idx = orc.topk(logits, cfg.top_k)
+            recs = [synth.make_record(seed, 0, int(e), H, I, cfg.bits_routed) for e in idx]
+            shared = synth.make_record(seed, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared)
+            t0 = time.perf_counter()
+            r = orc.route(router, cfg.router_dtype, gate, cfg.gate_dtype, xb, cfg.top_k, True)
+            ys = [orc.expert(rec, H, I, cfg.bits_routed, xb)[1] for rec in recs]
+            ysh = orc.expert(shared, H, I, cfg.bits_shared, xb)[1]
+            orc.combine(h_res.astype(np.float64), np.stack(ys), r["w"], ysh, r["sigma"])
+            times.append(time.perf_counter() - t0)
+            i += 1
+        return times
+
+    threads = orc.max_threads()
+    times = sample(budget_s, 5000)
+    orc.set_threads(1)
+    try:
+        one = sample(budget_s / 3.0, 6000)
+    finally:
+        orc.set_threads(threads)
     return dict(value=float(np.median(times) * 1e6), unit="us", cores=threads, kind="oracle",
                 sample=f"{len(times)} single-token layer decodes of the {cfg.name} workload "
-                       f"(fp64 oracle, OpenMP over output rows, weight generation excluded), median")
+                       f"(fp64 oracle, OpenMP over output rows, weight generation excluded), median",
+                value_1_core=float(np.median(one) * 1e6), sample_1_core=f"{len(one)} more decodes on one thread, median",
+                cpu_model=cpu_model())
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def bench_stack(cfg, args):
@@ -381,8 +405,55 @@ def bench_layer(cfg, args):
         one_pass()
     rec = moe.profile_end(n_launch)
     graph.destroy()
-    return ms_layer, rec, {"replay_us_per_layer_median": round(float(np.median(per)), 3),
-                           "replay_us_per_layer_p90": round(float(np.percentile(per, 90)), 3)}
+    extra = {"replay_us_per_layer_median": round(float(np.median(per)), 3),
+             "replay_us_per_layer_p90": round(float(np.percentile(per, 90)), 3)}
+    extra.update(launch_inclusive(layers, xs, hres, out, idx, w, ws, args))
+    return ms_layer, rec, extra
+
+
+def launch_inclusive(layers, xs, hres, out, idx, w, ws, args):
+    """Two companion figures of the rotation measurement.
+    one_layer_graph_us: one graph per layer instance, each replayed as its own
+    launch over the same rotation (so the launch overhead is included and the
+    data stay cold).  cache_warm_us_per_layer: one graph that calls the first
+    instance R times with the same x; its 40 MB then sit in the memory-side
+    cache, so this is a cache figure, not an HBM one."""
+    import torch
+    from bit_dequant_expert_route_amd import moe
+    R = len(layers)
+    s = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(s):
+        for i in range(R):
+            moe.capture_begin(s)
+            moe.layer_decode(layers[i], xs[i], hres[i], out, idx, w, ws, stream=s)
+            graphs.append(moe.capture_end(s))
+        moe.capture_begin(s)
+        for _ in range(R):
+            moe.layer_decode(layers[0], xs[0], hres[0], out, idx, w, ws, stream=s)
+        warm = moe.capture_end(s)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(args.steps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / args.steps / R
+
+    def each():
+        for g in graphs:
+            g.launch(s)
+
+    one = timed(each)
+    hot = timed(lambda: warm.launch(s))
+    for g in graphs:
+        g.destroy()
+    warm.destroy()
+    return {"one_layer_graph_us": round(one, 3), "cache_warm_us_per_layer": round(hot, 3)}
 
 
 def bench_tier(cfg, args):

@@ -40,6 +40,10 @@ class Oracle:
         self.path = path
         L = C.CDLL(path)
         self._L = L
+        L.oracle_set_threads.restype = None
+        L.oracle_set_threads.argtypes = [C.c_int]
+        L.oracle_max_threads.restype = C.c_int
+        L.oracle_max_threads.argtypes = []
         L.oracle_record_bytes.restype = C.c_size_t
         L.oracle_record_bytes.argtypes = [C.c_int, C.c_int, C.c_int]
         L.oracle_qmatvec.restype = None
@@ -145,6 +149,13 @@ class Oracle:
         out = np.empty_like(h_res)
         self._L.oracle_combine(h_res.size, w.size, h_res, y, w, y_shared, float(sigma), out)
         return out
+
+    def set_threads(self, n: int) -> None:
+        """Threads of the row loops; results are the same for any count."""
+        self._L.oracle_set_threads(int(n))
+
+    def max_threads(self) -> int:
+        return int(self._L.oracle_max_threads())
 
     def rmsnorm(self, h, eps: float = 1e-6):
         h = np.ascontiguousarray(h, dtype=np.float64)

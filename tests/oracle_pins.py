@@ -347,6 +347,24 @@ def pin_layer_dense(orc):
         assert abs(a["sigma"] - d["sigma"]) < 1e-15
 
 
+def pin_threads_bitwise(orc):
+    """The row loops run on several threads, each row summed by one thread in
+    its fixed order: every output is bitwise the same on one thread."""
+    rng = np.random.default_rng(26)
+    args = _tiny_layer_inputs(rng, E=16, K=4, H=512, I=256, bits_r=4, bits_s=2)
+    n = orc.max_threads()
+    many = orc.layer(renorm=True, **args)
+    orc.set_threads(1)
+    try:
+        one = orc.layer(renorm=True, **args)
+    finally:
+        orc.set_threads(n)
+    assert list(many["idx"]) == list(one["idx"])
+    for k in ("logits", "p", "w", "h", "y", "out"):
+        assert np.array_equal(np.asarray(many[k]), np.asarray(one[k])), k
+    assert many["sigma"] == one["sigma"]
+
+
 def pin_layer_all_selected(orc):
     """E = K: every expert is selected and (with renorm) the layer is the dense
     softmax mixture h_res + sum_e p_e y_e + sigma y_s (einsum brute force)."""
