@@ -208,11 +208,9 @@ int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in
   float *y_shared = reinterpret_cast<float *>(ws + wl.y_shared);
   float *x_stage = reinterpret_cast<float *>(ws + wl.x_stage);
   float *hres_stage = reinterpret_cast<float *>(ws + wl.hres_stage);
-  // each gate/up wave stages its chunks of x from x itself: reading the
-  // input is faster than waiting for a staging buffer the router kernel has
-  // just written (data written by the previous kernel come from memory)
-  uint32_t *xs_pairs = nullptr;
-  float *xs_sums = nullptr;
+  // each gate/up workgroup stages x from x itself: reading the input is
+  // faster than waiting for a staging buffer the router kernel has just
+  // written (data written by the previous kernel come from memory)
 
   // K1
   HeadParams hp = head_params(L, 1);
@@ -232,10 +230,6 @@ int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in
   const bool same_width = L->bits_shared == L->bits_routed;
   hp.n_shared_waves = same_width ? 0 : 1;  // launcher sizes it
   hp.bits_routed = L->bits_routed;
-  hp.xs_pairs = xs_pairs;
-  hp.xs_sums = xs_sums;
-  hp.xs_pair_stride = (int)wl.xs_pair_stride;
-  hp.xs_sum_stride = (int)wl.xs_sum_stride;
   MOE_TRY_HIP(timed(s, MOE_KERNEL_HEAD, [&] { return launch_head(hp, s); }), "router/shared launch");
 
   // K2
@@ -260,8 +254,6 @@ int layer_token(const moe_layer_t *L, int xsrc, const void *x, const float *h_in
   gp.w_out = w;
   gp.xsrc = xsrc == XS_BF16 ? XS_BF16 : XS_F32;
   gp.x = xsrc == XS_NORM ? static_cast<const void *>(x_stage) : x;
-  gp.xs_pairs = xs_pairs;
-  gp.xs_sums = xs_sums;
   gp.h_out = h_routed;
   gp.with_shared = same_width;
   gp.h_shared_out = h_shared;

@@ -352,6 +352,113 @@ __device__ __forceinline__ XStage<BITS, false> read_stage(const uint32_t *xs_pai
   return s;
 }
 
+// ---------------------------------------------------------------------------
+// x staged once per workgroup in LDS (the gate/up kernel).  Each thread loads
+// a slice of x, stages it into LDS, and after one barrier every wave reads
+// the chunks its lanes need: x crosses from L2 once per workgroup instead of
+// once per wave, and the bf16 staging math runs once per chunk.
+//   bf16 x: chunk c holds its staged pairs, the constant part and the column
+//           sum (kPairs + 2 words, rounded up to a multiple of 4 so that each
+//           chunk starts 16-byte aligned); thread kBlock - 1 - c stages it, so
+//           that wave 0 (which selects the experts) stages none while the
+//           chunks fit in the other waves.
+//   fp32 x: chunk c holds its columns, then kLdsPad floats of which the first
+//           is the column sum (the XS_LDSPAD layout); thread t stores the
+//           four columns 4t + 4 kBlock i.
+// ---------------------------------------------------------------------------
+// Whether the gate/up kernel stages x in LDS: when a wave's own chunks of x
+// would outweigh its weight rows (fp32 x, or 2-bit codes).  For 4-bit codes
+// and bf16 x (as many bytes of x as of weights per wave) each wave staging its
+// chunks itself was measured faster (q4 layer 21.5 against 21.8 us).
+__host__ __device__ constexpr bool gateup_x_in_lds(int bits, int xs) {
+  return xs != XS_BF16 || bits == 2;
+}
+
+template <int BITS, bool XF32>
+struct XLds {
+  static constexpr int kWords = XF32 ? ChunkGeom<BITS>::kCols + kLdsPad
+                                     : (ChunkGeom<BITS>::kPairs + 2 + 3) / 4 * 4;
+  static constexpr int kF4 = kMaxDim / (4 * kBlock);  // fp32: float4 per thread at most
+  static_assert(kMaxDim * BITS / 128 <= kBlock, "one bf16 chunk per thread");
+};
+
+template <int BITS, int XS>
+struct XPart;
+template <int BITS>
+struct XPart<BITS, XS_BF16> {
+  XRaw<BITS, XS_BF16> r;
+};
+template <int BITS>
+struct XPart<BITS, XS_F32> {
+  float4 v[XLds<BITS, true>::kF4];
+};
+
+template <int BITS, int XS>
+__device__ __forceinline__ void xpart_load(XPart<BITS, XS> &xp, const void *x, int H) {
+  const int t = threadIdx.x;
+  if constexpr (XS == XS_BF16) {
+    const int cpr = H / ChunkGeom<BITS>::kCols;
+    const int c = kBlock - 1 - t;
+    xp.r = load_raw<BITS, XS_BF16>(x, nullptr, c < cpr ? c : 0);
+  } else {
+    const float4 *xf = static_cast<const float4 *>(x);
+#pragma unroll
+    for (int i = 0; i < XLds<BITS, true>::kF4; ++i) {
+      const int q = i * kBlock + t;  // float4 index
+      xp.v[i] = xf[4 * q < H ? q : 0];
+    }
+  }
+}
+
+template <int BITS, int XS>
+__device__ __forceinline__ void xpart_store(const XPart<BITS, XS> &xp, uint32_t *xw, int H) {
+  const int t = threadIdx.x;
+  if constexpr (XS == XS_BF16) {
+    constexpr int NP = ChunkGeom<BITS>::kPairs;
+    const int c = kBlock - 1 - t;
+    if (c < H / ChunkGeom<BITS>::kCols) {
+      const XStage<BITS, false> s = stage_raw<BITS, XS_BF16>(xp.r);
+      uint32_t *d = xw + c * XLds<BITS, false>::kWords;
+#pragma unroll
+      for (int i = 0; i < NP / 4; ++i)
+        *reinterpret_cast<uint4 *>(d + 4 * i) = make_uint4(s.p[4 * i], s.p[4 * i + 1], s.p[4 * i + 2], s.p[4 * i + 3]);
+      *reinterpret_cast<float2 *>(d + NP) = make_float2(s.off, s.xs);
+    }
+  } else {
+    float *xl = reinterpret_cast<float *>(xw);
+#pragma unroll
+    for (int i = 0; i < XLds<BITS, true>::kF4; ++i) {
+      const int col = 4 * (i * kBlock + t);
+      // H is a multiple of 64, so a chunk's lanes agree on col < H
+      if (col < H) lds_put_chunk4<BITS>(xl, col, xp.v[i]);
+    }
+  }
+}
+
+// the staged chunk c as the dot products take it
+template <int BITS, bool XF32>
+__device__ __forceinline__ XStage<BITS, XF32> xlds_read(const uint32_t *xw, int c) {
+  if constexpr (XF32) {
+    return stage_raw<BITS, XS_LDSPAD>(load_raw<BITS, XS_LDSPAD>(nullptr, reinterpret_cast<const float *>(xw), c));
+  } else {
+    constexpr int NP = ChunkGeom<BITS>::kPairs;
+    const uint32_t *d = xw + c * XLds<BITS, false>::kWords;
+    XStage<BITS, false> s;
+#pragma unroll
+    for (int i = 0; i < NP / 4; ++i) {
+      const uint4 u = *reinterpret_cast<const uint4 *>(d + 4 * i);
+      s.p[4 * i + 0] = u.x;
+      s.p[4 * i + 1] = u.y;
+      s.p[4 * i + 2] = u.z;
+      s.p[4 * i + 3] = u.w;
+    }
+    const float2 sm = *reinterpret_cast<const float2 *>(d + NP);
+    s.off = sm.x;
+    s.xs = sm.y;
+    return s;
+  }
+}
+
 // lane layout over rows of `cols` columns at BITS bits
 struct RowMap {
   int cpr;      // 16-byte chunks per row

@@ -155,8 +155,6 @@ struct GateUpParams {
   float *w_out;
   int xsrc;                       // XS_BF16 or XS_F32
   const void *x;                  // [H]
-  const uint32_t *xs_pairs;       // staged x (XS_BF16), or null -> stage here
-  const float *xs_sums;
   float *h_out;                   // [n][I]
   // the shared expert's gate/up in the same launch (same width): its
   // workgroups come first and need no routing

@@ -125,6 +125,7 @@ __global__ __launch_bounds__(64) void k_topk(TopkParams p) {
 // ---------------------------------------------------------------------------
 template <int BITS, int NCH, int NPASS, int XS>
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
+  // each wave stages its own chunks of x (see gateup_x_in_lds)
   __shared__ int sel_ids[kMaxK];
   const int blk = wave_uniform(blockIdx.x);
   const int wv = wave_uniform(threadIdx.x >> 6);
@@ -149,22 +150,10 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
   const int row0 = wie * p.rows_per_wave;
   XStage<BITS, XF32> xs[NCH];
   XRaw<BITS, XS> xr[NCH];
-  bool from_buf = false;
-  if constexpr (XS == XS_BF16) from_buf = p.xs_pairs != nullptr;
-  if (from_buf) {
-    if constexpr (XS == XS_BF16) {
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int c = m.li + (j << m.lg);
-        xs[j] = read_stage<BITS>(p.xs_pairs, p.xs_sums, c < m.cpr ? c : 0);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = m.li + (j << m.lg);
-      xr[j] = load_raw<BITS, XS>(p.x, nullptr, c < m.cpr ? c : 0);
-    }
+  for (int j = 0; j < NCH; ++j) {
+    const int c = m.li + (j << m.lg);
+    xr[j] = load_raw<BITS, XS>(p.x, nullptr, c < m.cpr ? c : 0);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -200,9 +189,75 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
   GUTile<BITS, NCH, NPASS> tile;
   gu_load(tile, rec, shared ? p.soff : p.off, m, p.I, row0);
   __builtin_amdgcn_sched_barrier(0);
-  if (!from_buf) {
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) xs[j] = stage_raw<BITS, XS>(xr[j]);
+  for (int j = 0; j < NCH; ++j) xs[j] = stage_raw<BITS, XS>(xr[j]);
+  gu_compute(tile, xs, m, p.I, row0, valid, hout);
+}
+
+// K2 with x staged once per workgroup in LDS (XLds): the same work, for
+// shapes where a wave's own chunks of x would outweigh its weight rows
+template <int BITS, int NCH, int NPASS, int XS>
+__global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
+  // x of the workgroup (XLds layout), staged before the one barrier (every
+  // workgroup has it: the x of a wave comes from the others' parts)
+  extern __shared__ uint32_t xw[];
+  __shared__ int sel_ids[kMaxK];
+  constexpr bool XF32 = XS != XS_BF16;
+  const int blk = wave_uniform(blockIdx.x);
+  const int wv = wave_uniform(threadIdx.x >> 6);
+  const bool shared_blk = blk < p.n_shared_blocks;
+  // the shared expert does not depend on the routing: its workgroups come
+  // first and stream its rows while the routed ones are selecting experts
+  const int wave = shared_blk ? blk * (kBlock / 64) + wv
+                              : (blk - p.n_shared_blocks) * (kBlock / 64) + wv;
+  const int slot = shared_blk ? 0 : wave / p.waves_per_expert;
+  const int wie = shared_blk ? wave : wave - slot * p.waves_per_expert;
+  const bool topk = !shared_blk && !p.ids;  // workgroup-uniform
+  // a wave without rows still stages its part of x
+  const bool active = shared_blk ? wie < p.waves_per_expert : slot < p.n;
+
+  // Loads go out in the order they are needed (vmcnt counts in order): the
+  // logits (wave 0 of a routing workgroup), this thread's part of x, then
+  // the weights as soon as the expert is known.
+  float lv[kTopkNpl];
+  if (topk && wv == 0) topk_load(p.logits, p.E, lv);
+  const RowMap m = row_map<BITS>(p.H);
+  XPart<BITS, XS> xp;
+  xpart_load(xp, p.x, p.H);
+  const int row0 = wie * p.rows_per_wave;
+  GUTile<BITS, NCH, NPASS> tile;
+  bool valid = false;
+  // a list entry may name the shared expert: it still writes its own slot
+  float *const hout = shared_blk ? p.h_shared_out : p.h_out + (size_t)slot * p.I;
+  auto issue = [&](int id) {
+    const bool shared = id == kSharedId;
+    valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
+    const uint8_t *rec = shared ? p.shared_rec : p.experts + (size_t)(valid ? id : 0) * p.stride;
+    gu_load(tile, rec, shared ? p.soff : p.off, m, p.I, row0);
+  };
+  if (!topk && active) issue(shared_blk ? kSharedId : wave_uniform(p.ids[slot]));
+  __builtin_amdgcn_sched_barrier(0);
+  if (topk && wv == 0) {
+    int e;
+    float w;
+    // the selection gates every routed load of the workgroup: issue it
+    // ahead of the shared-expert waves computing on the same SIMD
+    __builtin_amdgcn_s_setprio(3);
+    topk_select(lv, p.E, p.K, p.renorm, e, w);
+    __builtin_amdgcn_s_setprio(0);
+    if (blk == p.n_shared_blocks) topk_store(e, w, p.K, p.idx_out, p.w_out);
+    if (lane_id() < p.K) sel_ids[lane_id()] = e;
+  }
+  xpart_store(xp, xw, p.H);
+  __syncthreads();
+  if (!active) return;
+  if (topk) issue(wave_uniform(sel_ids[slot]));
+  __builtin_amdgcn_sched_barrier(0);
+  XStage<BITS, XF32> xs[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = m.li + (j << m.lg);
+    xs[j] = xlds_read<BITS, XF32>(xw, c < m.cpr ? c : 0);
   }
   gu_compute(tile, xs, m, p.I, row0, valid, hout);
 }
@@ -760,9 +815,17 @@ hipError_t launch_gateup(const GateUpParams &p0, hipStream_t s) {
   p.n_shared_blocks = p.with_shared ? (p.waves_per_expert + 3) / 4 : 0;
   const int waves = p.waves_per_expert * p.n;
   const dim3 grid(p.n_shared_blocks + (waves + 3) / 4);
-#define MOE_GU(BITS, XS)                                                                    \
-  MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_gateup<BITS, NCH_, NP_, XS>), grid,         \
-                                              dim3(kBlock), 0, s, p))
+#define MOE_GU(BITS, XS)                                                                        \
+  do {                                                                                           \
+    if constexpr (gateup_x_in_lds(BITS, XS)) {                                                   \
+      const size_t lds = (size_t)(p.H * BITS / 128) * XLds<BITS, XS != XS_BF16>::kWords * 4;    \
+      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_gateup_xl<BITS, NCH_, NP_, XS>), grid,            \
+                                          dim3(kBlock), lds, s, p));                             \
+    } else {                                                                                     \
+      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_gateup<BITS, NCH_, NP_, XS>), grid, dim3(kBlock),  \
+                                          0, s, p));                                             \
+    }                                                                                            \
+  } while (0)
   if (p.bits == 4) {
     if (p.xsrc == XS_BF16) { MOE_GU(4, XS_BF16); } else { MOE_GU(4, XS_F32); }
   } else {
