@@ -351,7 +351,9 @@ def pin_threads_bitwise(orc):
     """The row loops run on several threads, each row summed by one thread in
     its fixed order: every output is bitwise the same on one thread."""
     rng = np.random.default_rng(26)
-    args = _tiny_layer_inputs(rng, E=16, K=4, H=512, I=256, bits_r=4, bits_s=2)
+    # one width and small records: the planted oracle mistakes that misread a
+    # record's size (tests/test_oracle_mutants.py) then stay inside its buffer
+    args = _tiny_layer_inputs(rng, E=8, K=2, H=128, I=64, bits_r=4, bits_s=4)
     n = orc.max_threads()
     many = orc.layer(renorm=True, **args)
     orc.set_threads(1)
