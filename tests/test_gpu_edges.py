@@ -1,9 +1,9 @@
 """Edge cases of the layer path against the oracle: the smallest and largest
 top-K (K = 1, K = E = 8), the largest expert count (E = 1024: the selection's
 second register width), rows that do not fill a wave's lanes (H, I multiples
-of 64 but not of 128), the widest rows (H = 8192: four chunks per lane), fp32
-activations with bf16 weights, the 64-token maximum, and run-to-run
-determinism."""
+of 64 but not of 128), the widest rows (H = 8192: four chunks per lane, also
+with fp32 x staged in LDS), fp32 activations with bf16 weights, the 64-token
+maximum, and run-to-run determinism."""
 import dataclasses
 
 import numpy as np
@@ -29,6 +29,10 @@ EDGE = {
     "ragged2": C("edge_ragged2", 192, 320, 16, 2, 2, 2, "f32", "bf16", "f32"),
     "wide4": C("edge_wide4", 8192, 64, 16, 2, 4, 4, "bf16", "bf16", "bf16"),
     "wide2": C("edge_wide2", 8192, 128, 16, 2, 2, 2, "bf16", "bf16", "bf16"),
+    # fp32 x at the widest rows: x staged per workgroup fills the most LDS
+    # (36 KB at 4 bits, 34 KB at 2 bits) and every thread holds eight float4
+    "wide4f": C("edge_wide4f", 8192, 64, 16, 2, 4, 4, "bf16", "bf16", "f32"),
+    "wide2f": C("edge_wide2f", 8192, 128, 16, 2, 2, 2, "bf16", "bf16", "f32"),
     "tall": C("edge_tall", 64, 8192, 16, 2, 4, 2, "f32", "f32", "f32"),
 }
 
