@@ -16,6 +16,7 @@ constexpr int kMaxDim = 8192;
 constexpr int kMaxTokens = 64;
 constexpr int kSharedId = -1;          // MOE_SHARED
 constexpr int kBlock = 256;            // threads per workgroup (4 waves)
+constexpr int kCUs = 256;              // compute units of an MI355X
 
 // where a kernel reads its activation vector from
 enum XSrc : int {
