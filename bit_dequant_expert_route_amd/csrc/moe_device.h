@@ -760,6 +760,153 @@ __device__ __forceinline__ void topk_select(float (&v)[kTopkNpl], int E, int K, 
   else topk_select_n<16>(v, K, renorm, e_out, w_out);
 }
 
+// ---------------------------------------------------------------------------
+// top-K by the four waves of a workgroup together (E <= 1024).  Wave w takes
+// the experts [w R, (w + 1) R) with R = 64 NPL, lane l the NPL consecutive
+// experts w R + NPL l + i (NPL = 2 for E <= 512, else 4).  Each wave finds its
+// own top K with the keyed-word rounds of topk_select8 and leaves them in LDS
+// with its softmax partial (its maximum and the sum of exp(l - maximum) over
+// its experts); after the workgroup's barrier every wave merges the 4 K
+// candidates itself.  The words carry the expert, so the merge orders equal
+// logits by the lower expert as the one-wave selection does.
+// ---------------------------------------------------------------------------
+struct TopkShare {
+  uint64_t cand[4][kMaxK];
+  float pmax[4], psum[4];
+};
+
+__device__ __forceinline__ int topk_npl(int E) { return E <= 256 * 2 ? 2 : 4; }
+
+template <int NPL>
+__device__ __forceinline__ void topk_part_load(const float *__restrict__ lg, int E, int w,
+                                               float (&v)[4]) {
+  const int e0 = (w * 64 + lane_id()) * NPL;
+  if ((E % NPL) == 0) {  // wave-uniform
+    if constexpr (NPL == 2) {
+      const float2 a = *reinterpret_cast<const float2 *>(lg + (e0 < E ? e0 : 0));
+      v[0] = a.x; v[1] = a.y;
+    } else {
+      const float4 a = *reinterpret_cast<const float4 *>(lg + (e0 < E ? e0 : 0));
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) v[i] = lg[e0 + i < E ? e0 + i : 0];
+  }
+}
+
+template <int NPL>
+__device__ __forceinline__ void topk_part_select(const float (&v)[4], int E, int K, int renorm,
+                                                 int w, TopkShare &sh) {
+  const int lane = lane_id();
+  const int e0 = (w * 64 + lane) * NPL;
+  uint64_t c[NPL];
+  float vl[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = e0 + i;
+    const uint32_t key = logit_key(v[i]);
+    c[i] = e < E ? ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
+    vl[i] = e < E ? key_logit(key) : -INFINITY;  // for the softmax partial
+  }
+#define MOE_CX(i, j)                          \
+  do {                                        \
+    const bool sw_ = c[j] > c[i];             \
+    const uint64_t t_ = sw_ ? c[j] : c[i];    \
+    c[j] = sw_ ? c[i] : c[j];                 \
+    c[i] = t_;                                \
+  } while (0)
+  if constexpr (NPL == 2) {
+    MOE_CX(0, 1);
+  } else {
+    MOE_CX(0, 1); MOE_CX(2, 3); MOE_CX(0, 2); MOE_CX(1, 3); MOE_CX(1, 2);
+  }
+#undef MOE_CX
+  uint32_t k0 = 0;
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    const uint32_t m = wave_max_u32((uint32_t)(c[0] >> 32));
+    const uint64_t b = __ballot((uint32_t)(c[0] >> 32) == m);
+    const int src = __builtin_ctzll(b);  // b != 0: m is some lane's key
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)c[0], src);
+    if (lane == 0) sh.cand[w][k] = ((uint64_t)m << 32) | lo;
+    if (lane == src) {  // shift the winner's list
+#pragma unroll
+      for (int i = 0; i < NPL - 1; ++i) c[i] = c[i + 1];
+      c[NPL - 1] = 0ull;
+    }
+    if (k == 0) k0 = m;
+  }
+  if (!renorm) {
+    // a wave without experts, or whose logits are all -inf, adds nothing
+    const float mx = k0 ? key_logit(k0) : -INFINITY;
+    float z = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) z += expf(vl[i] - mx);
+    }
+    z = seg_sum(z, 6);
+    if (lane == 0) {
+      sh.pmax[w] = mx;
+      sh.psum[w] = z;
+    }
+  }
+}
+
+// After the barrier: lane k < K comes back with the k-th selected expert
+// (descending logit, the lower expert first among equal ones; -2 if there is
+// none) in e_out; key_out holds its key and top_key the largest key, for
+// topk_merge_weight.
+__device__ __forceinline__ void topk_merge(const TopkShare &sh, int E, int K, int &e_out,
+                                           uint32_t &key_out, uint32_t &top_key) {
+  const int lane = lane_id();
+  const bool has = lane < 4 * K;
+  const int j = has ? lane : 0;  // candidate r of wave q, for lane j = q K + r
+  const uint64_t cw0 = sh.cand[j / K][j - (j / K) * K];
+  const uint64_t cw = has ? cw0 : 0ull;
+  uint32_t hi = (uint32_t)(cw >> 32), lo = (uint32_t)cw;
+  int my_e = -2;
+  uint32_t my_k = 0, k0 = 0;
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    const uint32_t m = wave_max_u32(hi);
+    const uint32_t ml = wave_max_u32(hi == m ? lo : 0u);
+    const uint64_t b = __ballot(hi == m && lo == ml);
+    const int src = __builtin_ctzll(b);  // the words are distinct: one lane
+    const uint32_t ex = 0xFFFFFFFFu - ml;
+    const int sel = (m != 0 && ex < (uint32_t)E) ? (int)ex : -2;
+    if (lane == src) hi = lo = 0u;
+    if (lane == k) {
+      my_k = m;
+      my_e = sel;
+    }
+    if (k == 0) k0 = m;
+  }
+  e_out = my_e;
+  key_out = my_k;
+  top_key = k0;
+}
+
+// The softmax weight of lane k's selection (lanes k < K; NaN elsewhere):
+// over the K selected logits (renorm), or over all E, from the waves' partials.
+__device__ __forceinline__ float topk_merge_weight(const TopkShare &sh, int K, int renorm, int e,
+                                                   uint32_t key, uint32_t top_key) {
+  const int lane = lane_id();
+  const float mx = key_logit(top_key);
+  const bool mine = lane < K && e >= 0;
+  const float t = mine ? expf(key_logit(key) - mx) : 0.f;
+  float den;
+  if (renorm) {
+    den = seg_sum(t, 6);
+  } else {
+    den = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (sh.pmax[w] != -INFINITY) den += sh.psum[w] * expf(sh.pmax[w] - mx);
+  }
+  return mine ? t / den : __builtin_nanf("");
+}
+
 // lanes 0..K-1 write the selection
 __device__ __forceinline__ void topk_store(int e, float w, int K, int32_t *idx, float *wout) {
   const int lane = lane_id();

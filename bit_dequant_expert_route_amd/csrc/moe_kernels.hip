@@ -126,7 +126,8 @@ __global__ __launch_bounds__(64) void k_topk(TopkParams p) {
 template <int BITS, int NCH, int NPASS, int XS>
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
   // each wave stages its own chunks of x (see gateup_x_in_lds)
-  __shared__ int sel_ids[kMaxK];
+  __shared__ TopkShare tsh;
+  static_assert(kBlock / 64 == 4, "the selection is split over four waves");
   const int blk = wave_uniform(blockIdx.x);
   const int wv = wave_uniform(threadIdx.x >> 6);
   const bool shared_blk = blk < p.n_shared_blocks;
@@ -139,12 +140,16 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
   const bool topk = !shared_blk && !p.ids;  // workgroup-uniform
   if (!topk && (shared_blk ? wie >= p.waves_per_expert : slot >= p.n)) return;
 
-  // Routing: wave 0 of the workgroup loads the logits and selects, the
-  // others wait at one barrier (one selection per workgroup, not per wave).
+  // Routing: the four waves of the workgroup each take a quarter of the
+  // logits, and after one barrier each merges the quarters' candidates.
   // Loads go out in the order they are needed (vmcnt counts in order):
   // logits, x, then the weights once the expert is known.
-  float lv[kTopkNpl];
-  if (topk && wv == 0) topk_load(p.logits, p.E, lv);
+  float lv[4];
+  const int npl = topk_npl(p.E);
+  if (topk) {
+    if (npl == 2) topk_part_load<2>(p.logits, p.E, wv, lv);
+    else topk_part_load<4>(p.logits, p.E, wv, lv);
+  }
   constexpr bool XF32 = XS != XS_BF16;
   const RowMap m = row_map<BITS>(p.H);
   const int row0 = wie * p.rows_per_wave;
@@ -159,25 +164,23 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
 
   int id;
   float *hout;
+  int sel_e = -2;
+  uint32_t sel_key = 0, top_key = 0;
   if (shared_blk) {
     id = kSharedId;
     hout = p.h_shared_out;
   } else {
     if (topk) {
-      if (wv == 0) {
-        int e;
-        float w;
-        // the selection gates every routed load of the workgroup: issue it
-        // ahead of the shared-expert waves computing on the same SIMD
-        __builtin_amdgcn_s_setprio(3);
-        topk_select(lv, p.E, p.K, p.renorm, e, w);
-        __builtin_amdgcn_s_setprio(0);
-        if (blk == p.n_shared_blocks) topk_store(e, w, p.K, p.idx_out, p.w_out);
-        if (lane_id() < p.K) sel_ids[lane_id()] = e;
-      }
+      // the selection gates every routed load of the workgroup: issue it
+      // ahead of the shared-expert waves computing on the same SIMD
+      __builtin_amdgcn_s_setprio(3);
+      if (npl == 2) topk_part_select<2>(lv, p.E, p.K, p.renorm, wv, tsh);
+      else topk_part_select<4>(lv, p.E, p.K, p.renorm, wv, tsh);
       __syncthreads();
       if (slot >= p.n) return;
-      id = wave_uniform(sel_ids[slot]);
+      topk_merge(tsh, p.E, p.K, sel_e, sel_key, top_key);
+      __builtin_amdgcn_s_setprio(0);
+      id = __builtin_amdgcn_readlane(sel_e, slot);
     } else {
       id = wave_uniform(p.ids[slot]);
     }
@@ -189,6 +192,10 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
   GUTile<BITS, NCH, NPASS> tile;
   gu_load(tile, rec, shared ? p.soff : p.off, m, p.I, row0);
   __builtin_amdgcn_sched_barrier(0);
+  // the first routed workgroup also reports the selection and its weights
+  if (topk && blk == p.n_shared_blocks && wv == 0)
+    topk_store(sel_e, topk_merge_weight(tsh, p.K, p.renorm, sel_e, sel_key, top_key), p.K,
+               p.idx_out, p.w_out);
 #pragma unroll
   for (int j = 0; j < NCH; ++j) xs[j] = stage_raw<BITS, XS>(xr[j]);
   gu_compute(tile, xs, m, p.I, row0, valid, hout);
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
   // x of the workgroup (XLds layout), staged before the one barrier (every
   // workgroup has it: the x of a wave comes from the others' parts)
   extern __shared__ uint32_t xw[];
-  __shared__ int sel_ids[kMaxK];
+  __shared__ TopkShare tsh;
   constexpr bool XF32 = XS != XS_BF16;
   const int blk = wave_uniform(blockIdx.x);
   const int wv = wave_uniform(threadIdx.x >> 6);
@@ -217,10 +224,14 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
   const bool active = shared_blk ? wie < p.waves_per_expert : slot < p.n;
 
   // Loads go out in the order they are needed (vmcnt counts in order): the
-  // logits (wave 0 of a routing workgroup), this thread's part of x, then
-  // the weights as soon as the expert is known.
-  float lv[kTopkNpl];
-  if (topk && wv == 0) topk_load(p.logits, p.E, lv);
+  // wave's quarter of the logits (routing workgroups), this thread's part of
+  // x, then the weights as soon as the expert is known.
+  float lv[4];
+  const int npl = topk_npl(p.E);
+  if (topk) {
+    if (npl == 2) topk_part_load<2>(p.logits, p.E, wv, lv);
+    else topk_part_load<4>(p.logits, p.E, wv, lv);
+  }
   const RowMap m = row_map<BITS>(p.H);
   XPart<BITS, XS> xp;
   xpart_load(xp, p.x, p.H);
@@ -237,22 +248,28 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
   };
   if (!topk && active) issue(shared_blk ? kSharedId : wave_uniform(p.ids[slot]));
   __builtin_amdgcn_sched_barrier(0);
-  if (topk && wv == 0) {
-    int e;
-    float w;
-    // the selection gates every routed load of the workgroup: issue it
-    // ahead of the shared-expert waves computing on the same SIMD
+  // the selection gates every routed load of the workgroup: issue it ahead
+  // of the shared-expert waves computing on the same SIMD
+  if (topk) {
     __builtin_amdgcn_s_setprio(3);
-    topk_select(lv, p.E, p.K, p.renorm, e, w);
-    __builtin_amdgcn_s_setprio(0);
-    if (blk == p.n_shared_blocks) topk_store(e, w, p.K, p.idx_out, p.w_out);
-    if (lane_id() < p.K) sel_ids[lane_id()] = e;
+    if (npl == 2) topk_part_select<2>(lv, p.E, p.K, p.renorm, wv, tsh);
+    else topk_part_select<4>(lv, p.E, p.K, p.renorm, wv, tsh);
   }
   xpart_store(xp, xw, p.H);
   __syncthreads();
   if (!active) return;
-  if (topk) issue(wave_uniform(sel_ids[slot]));
+  int sel_e = -2;
+  uint32_t sel_key = 0, top_key = 0;
+  if (topk) {
+    topk_merge(tsh, p.E, p.K, sel_e, sel_key, top_key);
+    __builtin_amdgcn_s_setprio(0);
+    issue(__builtin_amdgcn_readlane(sel_e, slot));
+  }
   __builtin_amdgcn_sched_barrier(0);
+  // the first routed workgroup also reports the selection and its weights
+  if (topk && blk == p.n_shared_blocks && wv == 0)
+    topk_store(sel_e, topk_merge_weight(tsh, p.K, p.renorm, sel_e, sel_key, top_key), p.K,
+               p.idx_out, p.w_out);
   XStage<BITS, XF32> xs[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
