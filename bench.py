@@ -86,16 +86,34 @@ def source_sha():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload, kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources."""
+def profile_summary(workload, kernel):
+    """The committed rocprofv3 counter summary of a kernel, if it was taken on
+    the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
     if d.get("source_sha") != source_sha():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d
+
+
+def traffic_from_profiles(workload, kernel):
+    """HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, scaled by the copy
+    probe) from the committed summary."""
+    d = profile_summary(workload, kernel)
+    return d.get("hbm_bytes_per_launch") if d else None
+
+
+def valu_from_profiles(workload, kernel, live_us):
+    """VALU issue bound of the kernel (SQ_INSTS_VALU x 4 cycles spread over the
+    1,024 SIMDs at 2.4 GHz) from the committed summary, and its share of the
+    kernel's live duration: which ceiling binds, next to the HBM roofline."""
+    d = profile_summary(workload, kernel)
+    if not d or d.get("valu_issue_us") is None:
+        return None
+    return {"instr_per_wave": d["valu_instr_per_wave"], "issue_bound_us": d["valu_issue_us"],
+            "live_us": round(live_us, 3), "frac": round(d["valu_issue_us"] / live_us, 4)}
 
 
 def build_rotation(cfg, R, seed0=1000):
@@ -677,6 +695,9 @@ def main():
                      "bytes_per_launch": dom_bytes},
         "cpu_baseline": None,
     }
+    valu = valu_from_profiles(args.workload, dom, kern_us[dom])
+    if valu:
+        line["valu_issue"] = {"kernel": dom_kernel, **valu}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
