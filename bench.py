@@ -81,7 +81,7 @@ def kernel_bytes(cfg):
 
 def source_sha():
     h = hashlib.sha256()
-    for f in ("moe_kernels.hip", "moe_device.h", "moe_api.cpp", "moe_internal.h"):
+    for f in ("moe_kernels.hip", "moe_device.h", "moe_api.cpp", "moe_internal.h", "moe_gdn.hip"):
         h.update(open(os.path.join(ROOT, "bit_dequant_expert_route_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -601,9 +601,12 @@ def main():
             "kernels_us": {"gdn_step": round(kern, 3)},
             "roofline": {"bound": "hbm", "kernel": "k_gdn_step", "achieved": round(achieved, 1),
                          "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
-                         "traffic": None, "bytes_per_launch": step_bytes},
+                         "traffic": traffic_from_profiles("gdn_step", "gdn"), "bytes_per_launch": step_bytes},
             "cpu_baseline": None,
         }
+        valu = valu_from_profiles("gdn_step", "gdn", kern)
+        if valu:
+            line["valu_issue"] = {"kernel": "k_gdn_step", **valu}
         print(json.dumps(line), flush=True)
         return
 
