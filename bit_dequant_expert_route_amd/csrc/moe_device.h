@@ -138,6 +138,35 @@ __device__ __forceinline__ void stage_chunk(const float (&v)[ChunkGeom<BITS>::kC
   s.xs = xs;
 }
 
+// the codes of one 16-byte chunk as the bf16 pairs chunk_dot2 forms (16 + q,
+// or 16 + 4q for the odd 2-bit fields), in the staged pairs' order
+template <int BITS>
+__device__ __forceinline__ void chunk_pairs(const uint4 &q, uint32_t magic,
+                                            uint32_t (&pr)[ChunkGeom<BITS>::kPairs]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t a3 = w[t] << 3, a1 = w[t] >> 1, a5 = w[t] >> 5, a9 = w[t] >> 9;
+    if constexpr (BITS == 4) {
+      constexpr uint32_t M = 0x00780078u;
+      pr[4 * t + 0] = (a3 & M) | magic;
+      pr[4 * t + 1] = (a1 & M) | magic;
+      pr[4 * t + 2] = (a5 & M) | magic;
+      pr[4 * t + 3] = (a9 & M) | magic;
+    } else {
+      constexpr uint32_t L = 0x00180018u, Hm = 0x00600060u;
+      pr[8 * t + 0] = (a3 & L) | magic;
+      pr[8 * t + 1] = (a3 & Hm) | magic;
+      pr[8 * t + 2] = (a1 & L) | magic;
+      pr[8 * t + 3] = (a1 & Hm) | magic;
+      pr[8 * t + 4] = (a5 & L) | magic;
+      pr[8 * t + 5] = (a5 & Hm) | magic;
+      pr[8 * t + 6] = (a9 & L) | magic;
+      pr[8 * t + 7] = (a9 & Hm) | magic;
+    }
+  }
+}
+
 // sum_c q_c * x_c over one 16-byte code chunk, for two chunks at once (two
 // independent accumulation chains: gate and up, or two rows)
 template <int BITS>

@@ -591,6 +591,8 @@ __device__ __forceinline__ XStage<BITS, XS != XS_BF16> group_stage_chunk(const G
   }
 }
 
+constexpr int kGroupTB = 4;  // tokens that share one unpacking of a code chunk
+
 // Work items are (group, block tile): the workgroup's four waves take
 // consecutive row tiles of one expert group, so the tokens' activations are
 // staged into LDS once per workgroup, tok_batch tokens at a time, and read
@@ -606,6 +608,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedParams p) {
   const int n_items = n_work_items(p, U);
   const RowMap m = row_map<BITS>(p.H);
   const int cpr = m.cpr;
+  const uint32_t magic = opaque(kMagic16);
   // the next item's weight rows are requested while this item's tokens are
   // worked through
   GUTile<BITS, NCH, NPASS> next;
@@ -642,17 +645,74 @@ __global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedParams p) {
       // activations are staged: loads complete in order, so requested
       // earlier they would hold up the staging
       if (i0 == 0 && item + (int)gridDim.x < n_items) fetch(item + gridDim.x, next, ngr, nrow0);
-      for (int b = 0; b < nb; ++b) {
-        Stage xs[NCH];
+      if constexpr (!XF32) {
+        // bf16 x: each code chunk is made into bf16 pairs once for up to
+        // kGroupTB tokens, which then take only the dot products (the same
+        // operations in the same order as gu_compute, token by token)
+        for (int b0 = 0; b0 < nb; b0 += kGroupTB) {
+          const int nt = nb - b0 < kGroupTB ? nb - b0 : kGroupTB;  // uniform
+          float a[kGroupTB][NPASS], u[kGroupTB][NPASS];
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-          const int c0 = m.li + (j << m.lg);
-          lds_load<BITS>(lds_x + (size_t)(b * cpr + (c0 < cpr ? c0 : 0)) * CS, xs[j]);
+          for (int t = 0; t < kGroupTB; ++t)
+#pragma unroll
+            for (int q = 0; q < NPASS; ++q) a[t][q] = u[t][q] = 0.f;
+#pragma unroll
+          for (int q = 0; q < NPASS; ++q) {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+              const bool in = in_tile(m, p.I, row0, q, j);
+              const uint32_t gsw = in ? tile.gs[q][j] : 0u, usw = in ? tile.us[q][j] : 0u;
+              uint32_t gpr[ChunkGeom<BITS>::kPairs], upr[ChunkGeom<BITS>::kPairs];
+              chunk_pairs<BITS>(tile.gq[q][j], magic, gpr);
+              chunk_pairs<BITS>(tile.uq[q][j], magic, upr);
+              const int c0 = m.li + (j << m.lg);
+              const int cc = c0 < cpr ? c0 : 0;
+#pragma unroll
+              for (int t = 0; t < kGroupTB; ++t) {
+                if (t < nt) {  // uniform
+                  Stage xs;
+                  lds_load<BITS>(lds_x + (size_t)((b0 + t) * cpr + cc) * CS, xs);
+                  float da = -xs.off, du = -xs.off;
+#pragma unroll
+                  for (int i = 0; i < ChunkGeom<BITS>::kPairs; ++i) {
+                    da = dot2bf(gpr[i], xs.p[i], da);
+                    du = dot2bf(upr[i], xs.p[i], du);
+                  }
+                  a[t][q] = fmaf(bf_lo(gsw), da, fmaf(bf_hi(gsw), xs.xs, a[t][q]));
+                  u[t][q] = fmaf(bf_lo(usw), du, fmaf(bf_hi(usw), xs.xs, u[t][q]));
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < kGroupTB; ++t) {
+            if (t < nt) {  // uniform
+              const int pair = __builtin_amdgcn_readlane(gr.pair, i0 + b0 + t);
+              const int tok = __builtin_amdgcn_readlane(gr.tok, i0 + b0 + t);
+              float *hout = gr.shared ? p.h_shared + (size_t)tok * p.I : p.h_routed + (size_t)pair * p.I;
+#pragma unroll
+              for (int q = 0; q < NPASS; ++q) {
+                const float sa = seg_sum(a[t][q], m.lg);
+                const float su = seg_sum(u[t][q], m.lg);
+                const int r = row0 + q * m.rpp + m.rip;
+                if (m.li == 0 && r < p.I) hout[r] = valid ? silu_mul(sa, su) : __builtin_nanf("");
+              }
+            }
+          }
         }
-        const int pair = __builtin_amdgcn_readlane(gr.pair, i0 + b);
-        const int tok = __builtin_amdgcn_readlane(gr.tok, i0 + b);
-        float *hout = gr.shared ? p.h_shared + (size_t)tok * p.I : p.h_routed + (size_t)pair * p.I;
-        gu_compute(tile, xs, m, p.I, row0, valid, hout);
+      } else {
+        for (int b = 0; b < nb; ++b) {
+          Stage xs[NCH];
+#pragma unroll
+          for (int j = 0; j < NCH; ++j) {
+            const int c0 = m.li + (j << m.lg);
+            lds_load<BITS>(lds_x + (size_t)(b * cpr + (c0 < cpr ? c0 : 0)) * CS, xs[j]);
+          }
+          const int pair = __builtin_amdgcn_readlane(gr.pair, i0 + b);
+          const int tok = __builtin_amdgcn_readlane(gr.tok, i0 + b);
+          float *hout = gr.shared ? p.h_shared + (size_t)tok * p.I : p.h_routed + (size_t)pair * p.I;
+          gu_compute(tile, xs, m, p.I, row0, valid, hout);
+        }
       }
     }
   }
