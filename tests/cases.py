@@ -76,9 +76,11 @@ def _x_from_hres(orc, h_res, dtype):
 
 def make_layer_case(cfg: synth.LayerConfig, seed: int, renorm: bool = True,
                     orc: oracle.Oracle | None = None, records_from=None,
-                    bits_shared: int | None = None) -> LayerCase:
+                    bits_shared: int | None = None, router_edit=None) -> LayerCase:
     """`records_from(expert_id) -> bytes` overrides the generator (tests that
-    plant special experts)."""
+    plant special experts).  `router_edit(router, logits) -> router` changes
+    the router once the first draw's logits are known (tests that plant exact
+    ties); the logit-gap rule is then not applied."""
     orc = orc or oracle.get()
     bits_shared = bits_shared or cfg.bits_shared
     router = synth.router_weights(cfg, seed)
@@ -91,6 +93,9 @@ def make_layer_case(cfg: synth.LayerConfig, seed: int, renorm: bool = True,
         else:
             x, x64 = _x_from_hres(orc, h_res, cfg.x_dtype)
         logits = orc.router(router, cfg.router_dtype, x64)
+        if router_edit is not None:
+            router = router_edit(router, logits)
+            break
         if logit_gap(logits, cfg.top_k) >= GAP:
             break
     else:
