@@ -287,18 +287,28 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
 // holds its precomputed down output.  WAVES: waves per workgroup; each
 // workgroup stages all K + 1 SwiGLU vectors, so eight waves halve those L2
 // reads per weight byte where the grid still gives every CU a workgroup.
-template <int BITS, int NCH, int NPASS, int MAXK, bool SHARED_IN, bool USE_LDS, int WAVES>
+// SPLIT: where the rows give fewer waves than that, two waves share each set
+// of rows, one taking the first half of the experts (the shared one first)
+// and the other the rest; their partial sums meet in LDS.
+template <int BITS, int NCH, int NPASS, int MAXK, bool SHARED_IN, bool USE_LDS, int WAVES, bool SPLIT>
 __global__ __launch_bounds__(64 * WAVES) void k_down_combine(DownParams p) {
   constexpr int kThreads = 64 * WAVES;
+  static_assert(!SPLIT || WAVES % 2 == 0, "waves pair up");
   // [K (+1)][I]: the SwiGLU outputs, staged once, each code chunk's columns
   // followed by kLdsPad unused floats
   extern __shared__ float hl[];
   constexpr int XSH = USE_LDS ? XS_LDSPAD : XS_F32;
   constexpr int NC = ChunkGeom<BITS>::kCols;
-  const int wave = wave_uniform(blockIdx.x * (WAVES) + (threadIdx.x >> 6));
+  const int wv = wave_uniform(threadIdx.x >> 6);
+  const int wave = wave_uniform(SPLIT ? blockIdx.x * (WAVES / 2) + (wv >> 1) : blockIdx.x * WAVES + wv);
+  const int half = SPLIT ? (wv & 1) : 0;
   const RowMap m = row_map<BITS>(p.I);
   const int row0 = wave * p.rows_per_wave;
   const bool active = row0 < p.H;
+  // experts in order: the shared one (if here), then the routed ones
+  constexpr int SIN = SHARED_IN ? 1 : 0;
+  const int n_first = (p.K + SIN + 1) / 2;
+  auto mine = [&](int slot) { return !SPLIT || ((slot < n_first) == (half == 0)); };
 
   // Loads in the order their data are needed (vmcnt counts in order): the
   // selection, the shared expert's rows (known before the selection), the
@@ -313,7 +323,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_down_combine(DownParams p) {
     wk[k] = k < p.K ? p.w[k] : 0.f;
   }
   DnTile<BITS, NCH, NPASS> ts;
-  if constexpr (SHARED_IN) down_load(ts, p.shared_rec, p.soff, p.H, m, row0);
+  if constexpr (SHARED_IN) {
+    if (mine(0)) down_load(ts, p.shared_rec, p.soff, p.H, m, row0);
+  }
   const int lds_stride = (p.I / NC) * (NC + kLdsPad);  // floats per expert in LDS
   // float4 per thread held in registers (8192 values); the rest, if any, go
   // through a plain loop after the barrier's other loads
@@ -334,7 +346,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_down_combine(DownParams p) {
   DnTile<BITS, NCH, NPASS> t[MAXK];
 #pragma unroll
   for (int k = 0; k < MAXK; ++k) {
-    if (k < p.K) {  // wave-uniform
+    if (k < p.K && mine(k + SIN)) {  // wave-uniform
       ids[k] = wave_uniform(ids[k]);
       const bool v = ids[k] >= 0 && ids[k] < p.E;
       down_load(t[k], p.experts + (size_t)(v ? ids[k] : 0) * p.stride, p.off, p.H, m, row0);
@@ -362,7 +374,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_down_combine(DownParams p) {
     }
     __syncthreads();
   }
-  if (!active) return;
+  // (split pairs meet at a second barrier: their waves stay to the end; rows
+  // past H are masked where they are loaded and stored)
+  if (!SPLIT && !active) return;
   const int hstride = USE_LDS ? lds_stride : p.I;
   const float *hr = USE_LDS ? hl : p.h_routed;
   const float *hs = USE_LDS ? hl + (size_t)p.K * lds_stride : p.h_shared;
@@ -371,14 +385,26 @@ __global__ __launch_bounds__(64 * WAVES) void k_down_combine(DownParams p) {
 #pragma unroll
   for (int i = 0; i < NPASS; ++i) acc[i] = 0.f;
   const float sig = p.sigma[0];
-  if constexpr (SHARED_IN)
-    down_accumulate<BITS, NCH, NPASS, XSH>(hs, m, p.H, row0, true, sig, ts, acc);
+  if constexpr (SHARED_IN) {
+    if (mine(0)) down_accumulate<BITS, NCH, NPASS, XSH>(hs, m, p.H, row0, true, sig, ts, acc);
+  }
 #pragma unroll
   for (int k = 0; k < MAXK; ++k) {
-    if (k < p.K) {
+    if (k < p.K && mine(k + SIN)) {
       const bool v = ids[k] >= 0 && ids[k] < p.E;
       down_accumulate<BITS, NCH, NPASS, XSH>(hr + (size_t)k * hstride, m, p.H, row0, v, wk[k], t[k], acc);
     }
+  }
+  if constexpr (SPLIT) {
+    __shared__ float part[WAVES / 2][NPASS][64];
+    if (half) {
+#pragma unroll
+      for (int i = 0; i < NPASS; ++i) part[wv >> 1][i][lane_id()] = acc[i];
+    }
+    __syncthreads();
+    if (half || !active) return;
+#pragma unroll
+    for (int i = 0; i < NPASS; ++i) acc[i] += part[wv >> 1][i][lane_id()];
   }
 #pragma unroll
   for (int i = 0; i < NPASS; ++i) {
@@ -935,17 +961,20 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
     // eight-wave workgroups when there are enough waves for one per CU (q4
     // layer: 20.85 against 21.15 us; with 1024 waves, half the CUs would idle)
     const bool eight = use_lds && waves >= 8 * kCUs;
-    const dim3 grid(eight ? (waves + 7) / 8 : (waves + 3) / 4);
+    // otherwise (fewer rows) two waves share each set of rows, splitting the
+    // experts, so that the grid still has waves to hide latency with
+    const bool split = use_lds && !eight;
+    const dim3 grid(eight ? (waves + 7) / 8 : (split ? (waves + 1) / 2 : (waves + 3) / 4));
 #define MOE_DC(BITS, MAXK, SIN)                                                                       \
   do {                                                                                                \
     if (eight)                                                                                        \
-      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, true, 8>),     \
+      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, true, 8, false>), \
                                           grid, dim3(512), lds, s, p));                               \
-    else if (use_lds)                                                                                 \
-      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, true, 4>),     \
+    else if (split)                                                                                   \
+      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, true, 4, true>), \
                                           grid, dim3(kBlock), lds, s, p));                            \
     else                                                                                              \
-      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, false, 4>),    \
+      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, false, 4, false>), \
                                           grid, dim3(kBlock), 0, s, p));                              \
   } while (0)
     if (bits == 4) {
