@@ -565,7 +565,7 @@ def read_peak_gbps():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the hot path is a single-GPU "
+        print(json.dumps({"error": "the benchmark runs on one GPU only: the hot path is a single-GPU "
                                    "kernel sequence with no sharding or collectives; run with --gpus 1"}))
         sys.exit(2)
     import torch
