@@ -39,12 +39,16 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
   extern __shared__ float xl[];
   const int wv = wave_uniform(threadIdx.x >> 6);
   const int blk = wave_uniform(blockIdx.x);
+  // waves per workgroup: two where every wave only reads its row (the 513
+  // rows of a token then reach all 256 CUs), four with the norm prologue or
+  // the shared expert's rows
+  const int wpb = (int)(blockDim.x / 64);
   // the stack path normalises x in every workgroup: the router row is
   // requested first so that its latency overlaps the normalisation
   RowPre pre{};
   bool have_pre = false;
   if constexpr (XS == XS_NORM) {
-    const int unit = blk * (kBlock / 64) + wv;
+    const int unit = blk * wpb + wv;
     const int row = unit - (unit / (p.E + 1)) * (p.E + 1);
     if (blk < p.n_router_blocks && unit < p.T * (p.E + 1) && row < p.E) {
       const size_t esz = p.router_dtype == 1 ? 2 : 4;
@@ -55,7 +59,7 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
     norm_prologue(p, xl);
   }
   if (blk < p.n_router_blocks) {
-    const int unit = blk * (kBlock / 64) + wv;  // (token, row) pairs, then one x stager per token
+    const int unit = blk * wpb + wv;  // (token, row) pairs, then one x stager per token
     const int rows = p.E + 1;
     if (unit >= p.T * rows) {
       const int st = unit - p.T * rows;
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
     return;
   }
   if constexpr (BITS_S != 0) {
-    const int sw = (blk - p.n_router_blocks) * (kBlock / 64) + wv;
+    const int sw = (blk - p.n_router_blocks) * wpb + wv;
     if (sw >= p.n_shared_waves) return;
     constexpr bool XF32 = XS != XS_BF16;
     const RowMap m = row_map<BITS_S>(p.H);
@@ -881,7 +885,10 @@ hipError_t launch_head(const HeadParams &p0, hipStream_t s) {
     p.n_shared_waves = (p.I + p.shared_rows_per_wave - 1) / p.shared_rows_per_wave;
   }
   const int units = p.T * (p.E + 1) + p.T;  // rows of every token, then one x stager per token
-  p.n_router_blocks = (units + 3) / 4;
+  // two waves per workgroup unless the norm prologue or the shared expert's
+  // rows run here (q4 layer: 20.64 -> 20.50 us per layer)
+  const int W = (bs == 0 && p.xsrc != XS_NORM) ? 2 : 4;
+  p.n_router_blocks = (units + W - 1) / W;
   const int nsb = bs ? (p.n_shared_waves + 3) / 4 : 0;
   const dim3 grid(p.n_router_blocks + nsb);
   const size_t lds = p.xsrc == XS_NORM ? (size_t)p.H * sizeof(float) : 0;
@@ -893,7 +900,7 @@ hipError_t launch_head(const HeadParams &p0, hipStream_t s) {
     MOE_DISPATCH(nch, npass,                                                                     \
                  MOE_LAUNCH((k_head<XS, 2, NCH_, NP_>), grid, dim3(kBlock), lds, s, p)); \
   } else {                                                                                       \
-    MOE_LAUNCH((k_head<XS, 0, 1, 1>), grid, dim3(kBlock), lds, s, p);                    \
+    MOE_LAUNCH((k_head<XS, 0, 1, 1>), grid, dim3(64 * W), lds, s, p);                    \
   }
   if (p.xsrc == XS_BF16) {
     MOE_HEAD(XS_BF16)
