@@ -1109,6 +1109,64 @@ __device__ __forceinline__ void norm_prologue(const HeadParams &p, float *xl) {
   __syncthreads();
 }
 
+// The same normalisation for workgroups that only take dot products with x:
+// x = v r with v = h + u and the scalar r = 1 / sqrt(mean(v^2) + eps), so a
+// row's dot with x is r times its dot with v.  v goes to LDS in the pass that
+// sums its squares, and one barrier serves both; workgroup 0 still writes the
+// normalised x (and v) for the next kernels.  Returns r.
+__device__ __forceinline__ float norm_prologue_scaled(const HeadParams &p, float *vl) {
+  __shared__ float red[kBlock / 64];
+  constexpr int kSteps = kMaxDim / (4 * kBlock);
+  const int H = p.H;
+  float4 hv[kSteps];
+  uint2 uv[kSteps];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int c = (i * kBlock + threadIdx.x) * 4;
+    const int cc = c < H ? c : 0;
+    hv[i] = *reinterpret_cast<const float4 *>(p.h_in + cc);
+    uv[i] = p.upd ? *reinterpret_cast<const uint2 *>(p.upd + cc) : make_uint2(0u, 0u);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int c = (i * kBlock + threadIdx.x) * 4;
+    if (c < H) {
+      float4 v = hv[i];
+      v.x += bf_lo(uv[i].x);
+      v.y += bf_hi(uv[i].x);
+      v.z += bf_lo(uv[i].y);
+      v.w += bf_hi(uv[i].y);
+      hv[i] = v;
+      ss = fmaf(v.x, v.x, ss);
+      ss = fmaf(v.y, v.y, ss);
+      ss = fmaf(v.z, v.z, ss);
+      ss = fmaf(v.w, v.w, ss);
+      *reinterpret_cast<float4 *>(vl + c) = v;
+    }
+  }
+  ss = seg_sum(ss, 6);
+  if (lane_id() == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kBlock / 64; ++i) tot += red[i];
+  const float rinv = 1.0f / sqrtf(tot / (float)H + 1e-6f);
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      const int c = (i * kBlock + threadIdx.x) * 4;
+      if (c < H) {
+        const float4 v = hv[i];
+        if (p.hres_out) *reinterpret_cast<float4 *>(p.hres_out + c) = v;
+        if (p.x_out)
+          *reinterpret_cast<float4 *>(p.x_out + c) = make_float4(v.x * rinv, v.y * rinv, v.z * rinv, v.w * rinv);
+      }
+    }
+  }
+  return rinv;
+}
+
 // one wave stages bf16 x for every chunk of a row at BITS and stores it
 template <int BITS>
 __device__ __forceinline__ void write_xstage(const void *x, int H, uint32_t *pairs, float *sums) {

@@ -47,6 +47,9 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
   // requested first so that its latency overlaps the normalisation
   RowPre pre{};
   bool have_pre = false;
+  // the dots of the rows are taken with h + u and scaled by the norm's
+  // reciprocal when only dots read x here (no shared expert's rows)
+  float rscale = 1.0f;
   if constexpr (XS == XS_NORM) {
     const int unit = blk * wpb + wv;
     const int row = unit - (unit / (p.E + 1)) * (p.E + 1);
@@ -56,7 +59,8 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
                          p.router_dtype, p.H);
       have_pre = true;
     }
-    norm_prologue(p, xl);
+    if constexpr (BITS_S == 0) rscale = norm_prologue_scaled(p, xl);
+    else norm_prologue(p, xl);
   }
   if (blk < p.n_router_blocks) {
     const int unit = blk * wpb + wv;  // (token, row) pairs, then one x stager per token
@@ -79,10 +83,10 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
     if (row < p.E) {
       const size_t esz = p.router_dtype == 1 ? 2 : 4;
       const void *wrow = static_cast<const uint8_t *>(p.router) + (size_t)row * p.H * esz;
-      const float d = row_dot<XS>(wrow, p.router_dtype, p.H, p.x, xl, t, pre, have_pre);
+      const float d = row_dot<XS>(wrow, p.router_dtype, p.H, p.x, xl, t, pre, have_pre) * rscale;
       if (lane_id() == 0) p.logits[(size_t)t * p.E + row] = d;
     } else {
-      const float d = row_dot<XS>(p.gvec, p.gate_dtype, p.H, p.x, xl, t);
+      const float d = row_dot<XS>(p.gvec, p.gate_dtype, p.H, p.x, xl, t) * rscale;
       if (lane_id() == 0) p.sigma[t] = 1.0f / (1.0f + expf(-d));
     }
     return;
