@@ -16,6 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 SOURCES = [os.path.join(CSRC, "moe_kernels.hip"), os.path.join(CSRC, "moe_util.hip"),
            os.path.join(CSRC, "moe_gdn.hip"), os.path.join(CSRC, "moe_api.cpp")]
 HEADERS = [os.path.join(CSRC, "moe_internal.h"), os.path.join(CSRC, "moe_device.h"),
+           os.path.join(CSRC, "moe_sortnet.h"),
            os.path.join(os.path.dirname(HERE), "include", "moe.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -446,7 +446,8 @@ int moe_route(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void 
   if (!topk_idx || !topk_w || !shared_sigma) return fail(MOE_EINVAL, "an output pointer is NULL");
   if (!aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(shared_sigma, 4))
     return fail(MOE_EALIGN, "outputs must be 4-byte aligned");
-  if (logits && !aligned(logits, 4)) return fail(MOE_EALIGN, "logits must be 4-byte aligned");
+  // the top-K kernel reads the logits with 16-byte loads
+  if (logits && !aligned(logits, 16)) return fail(MOE_EALIGN, "logits must be 16-byte aligned");
   const WsLayout wl = ws_layout(L, n_tokens, 0);
   if ((st = check_ws(ws, ws_bytes, wl.total)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -612,9 +613,10 @@ int layer_batch(const moe_layer_t *L, int T, int xsrc, const void *x, const floa
   return MOE_OK;
 }
 
-int moe_layer_decode(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void *x,
-                     const float *h_res, float *h_out, int32_t *topk_idx, float *topk_w,
-                     void *ws, size_t ws_bytes, void *stream) {
+// the arguments of a layer decode other than its workspace
+static int check_decode_args(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void *x,
+                             const float *h_res, const float *h_out, const int32_t *topk_idx,
+                             const float *topk_w) {
   int st;
   if ((st = check_layer(L)) != MOE_OK) return st;
   if ((st = check_tokens(n_tokens)) != MOE_OK) return st;
@@ -625,6 +627,15 @@ int moe_layer_decode(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, cons
   if (h_out == h_res) return fail(MOE_EINVAL, "h_out may not alias h_res");
   if (!topk_idx || !topk_w) return fail(MOE_EINVAL, "topk_idx / topk_w is NULL");
   if (!aligned(topk_idx, 4) || !aligned(topk_w, 4)) return fail(MOE_EALIGN, "topk outputs must be 4-byte aligned");
+  return MOE_OK;
+}
+
+int moe_layer_decode(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void *x,
+                     const float *h_res, float *h_out, int32_t *topk_idx, float *topk_w,
+                     void *ws, size_t ws_bytes, void *stream) {
+  int st;
+  if ((st = check_decode_args(L, n_tokens, x_dtype, x, h_res, h_out, topk_idx, topk_w)) != MOE_OK)
+    return st;
   const WsLayout wl = ws_layout(L, n_tokens, 0);
   if ((st = check_ws(ws, ws_bytes, wl.total)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -707,7 +718,7 @@ struct moe_tier_s {
   std::vector<int32_t> owner;    // slot -> expert, or -1
   std::vector<uint64_t> used;    // slot -> tick of its last use (0: never)
   uint64_t tick = 0, hits = 0, misses = 0, bytes = 0;
-  int32_t *pinned = nullptr;     // page-locked: [kMaxK] routed ids, [kMaxK] their slots
+  int32_t routing[2 * kMaxK];    // the routed ids read back, then their slots
   std::mutex mu;
 };
 
@@ -735,7 +746,6 @@ int moe_tier_create(const void *host_records, int n_experts, size_t expert_strid
 
 int moe_tier_destroy(moe_tier_t t) {
   if (!t) return fail(MOE_EINVAL, "tier is NULL");
-  if (t->pinned) (void)hipHostFree(t->pinned);
   delete t;
   return MOE_OK;
 }
@@ -840,15 +850,9 @@ int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype,
   tp.w = topk_w;
   MOE_TRY_HIP(timed(s, MOE_KERNEL_TOPK, [&] { return launch_topk(tp, s); }), "top-K launch");
 
-  // the routing on the host, then the missing records into their slots (the
-  // previous call's copies from the page-locked buffer ended at this wait)
-  if (!t->pinned) {  // first call: the page-locked routing buffer (host memory)
-    void *pin = nullptr;
-    MOE_TRY_HIP(hipHostMalloc(&pin, 2 * kMaxK * sizeof(int32_t), hipHostMallocDefault),
-                "hipHostMalloc (routing buffer)");
-    t->pinned = static_cast<int32_t *>(pin);
-  }
-  int32_t *ids = t->pinned, *slots = t->pinned + kMaxK;
+  // the routing on the host (read back into the tier object), then the
+  // missing records into their slots
+  int32_t *ids = t->routing, *slots = t->routing + kMaxK;
   int32_t miss[kMaxK];
   MOE_TRY_HIP(hipMemcpyAsync(ids, topk_idx, K * sizeof(int32_t), hipMemcpyDeviceToHost, s), "routing copy");
   MOE_TRY_HIP(hipStreamSynchronize(s), "waiting for the routing");

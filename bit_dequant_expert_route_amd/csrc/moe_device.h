@@ -5,6 +5,7 @@
 #pragma once
 
 #include "moe_internal.h"
+#include "moe_sortnet.h"
 
 #include <math.h>
 #include <stdint.h>
@@ -718,10 +719,10 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // E <= 512 (lane-contiguous layout of topk_load).  Each logit becomes the
 // 64-bit word (key << 32) | (2^32 - 1 - expert): a larger word is a larger
 // logit, or an equal logit with a lower expert.  Every lane sorts its 8 words
-// with a 19-comparator, depth-6 sorting network; each of the K rounds is then
-// a wave maximum of the lanes' first keys, the lowest lane holding it (lanes
-// own increasing expert ranges, so that is the lowest expert among equal
-// logits) and a shift of that lane's list.
+// with the 19-comparator, depth-6 network of moe_sortnet.h; each of the K
+// rounds is then a wave maximum of the lanes' first keys, the lowest lane
+// holding it (lanes own increasing expert ranges, so that is the lowest
+// expert among equal logits) and a shift of that lane's list.
 __device__ __forceinline__ void topk_select8(float (&v)[kTopkNpl], int E, int K, int renorm,
                                              int &e_out, float &w_out) {
   const int lane = lane_id();
@@ -739,12 +740,8 @@ __device__ __forceinline__ void topk_select8(float (&v)[kTopkNpl], int E, int K,
     c[j] = sw_ ? c[i] : c[j];                 \
     c[i] = t_;                                \
   } while (0)
-  MOE_CX(0, 2); MOE_CX(1, 3); MOE_CX(4, 6); MOE_CX(5, 7);
-  MOE_CX(0, 4); MOE_CX(1, 5); MOE_CX(2, 6); MOE_CX(3, 7);
-  MOE_CX(0, 1); MOE_CX(2, 3); MOE_CX(4, 5); MOE_CX(6, 7);
-  MOE_CX(2, 4); MOE_CX(3, 5);
-  MOE_CX(1, 4); MOE_CX(3, 6);
-  MOE_CX(1, 2); MOE_CX(3, 4); MOE_CX(5, 6);
+#pragma unroll
+  for (int q = 0; q < kSort8Comparators; ++q) MOE_CX(kSort8Net[q][0], kSort8Net[q][1]);
 #undef MOE_CX
   uint32_t my_k = 0;
   int my_e = -2;

@@ -194,11 +194,15 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
     }
     hout = p.h_out + (size_t)slot * p.I;
   }
+  // an entry whose record cannot be read at this width (an id out of range,
+  // or the shared expert at another width) reads routed record 0 with the
+  // routed geometry, so every load stays inside the records, and yields NaN
   const bool shared = id == kSharedId;
   const bool valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
-  const uint8_t *rec = shared ? p.shared_rec : p.experts + (size_t)(valid ? id : 0) * p.stride;
+  const bool from_shared = shared && valid;
+  const uint8_t *rec = from_shared ? p.shared_rec : p.experts + (size_t)(valid && !shared ? id : 0) * p.stride;
   GUTile<BITS, NCH, NPASS> tile;
-  gu_load(tile, rec, shared ? p.soff : p.off, m, p.I, row0);
+  gu_load(tile, rec, from_shared ? p.soff : p.off, m, p.I, row0);
   __builtin_amdgcn_sched_barrier(0);
   // the first routed workgroup also reports the selection and its weights
   if (topk && blk == p.n_shared_blocks && wv == 0)
@@ -249,10 +253,12 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
   // a list entry may name the shared expert: it still writes its own slot
   float *const hout = shared_blk ? p.h_shared_out : p.h_out + (size_t)slot * p.I;
   auto issue = [&](int id) {
+    // unreadable entries (see k_gateup) read routed record 0 and yield NaN
     const bool shared = id == kSharedId;
     valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
-    const uint8_t *rec = shared ? p.shared_rec : p.experts + (size_t)(valid ? id : 0) * p.stride;
-    gu_load(tile, rec, shared ? p.soff : p.off, m, p.I, row0);
+    const bool from_shared = shared && valid;
+    const uint8_t *rec = from_shared ? p.shared_rec : p.experts + (size_t)(valid && !shared ? id : 0) * p.stride;
+    gu_load(tile, rec, from_shared ? p.soff : p.off, m, p.I, row0);
   };
   if (!topk && active) issue(shared_blk ? kSharedId : wave_uniform(p.ids[slot]));
   __builtin_amdgcn_sched_barrier(0);
@@ -439,11 +445,13 @@ __global__ __launch_bounds__(kBlock) void k_down_y(DownParams p) {
   const int row0 = wie * p.rows_per_wave;
   // a null id list selects the shared expert for every slot
   const int id = p.ids ? wave_uniform(p.ids[slot]) : kSharedId;
+  // unreadable entries (see k_gateup) read routed record 0 and yield NaN
   const bool shared = id == kSharedId;
   const bool valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
-  const uint8_t *rec = shared ? p.shared_rec : p.experts + (size_t)(valid ? id : 0) * p.stride;
+  const bool from_shared = shared && valid;
+  const uint8_t *rec = from_shared ? p.shared_rec : p.experts + (size_t)(valid && !shared ? id : 0) * p.stride;
   DnTile<BITS, NCH, NPASS> t;
-  down_load(t, rec, shared ? p.soff : p.off, p.H, m, row0);
+  down_load(t, rec, from_shared ? p.soff : p.off, p.H, m, row0);
   float acc[NPASS];
 #pragma unroll
   for (int i = 0; i < NPASS; ++i) acc[i] = 0.f;

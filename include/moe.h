@@ -106,7 +106,9 @@ const char *moe_last_error(void);
 int moe_abi_version(void);
 
 /* Bytes of one quantised [rows][cols] matrix: codes plus sb words, each
- * section rounded up to 256 bytes.  0 when the shape is invalid. */
+ * section rounded up to 256 bytes ([a2a-fr] "FMA-optimised dequantisation
+ * kernels": b-bit codes with a scale and a bias per group of inputs).  0 when
+ * the shape is invalid. */
 size_t moe_qmatrix_bytes(int rows, int cols, int bits, int group);
 /* Bytes of one expert record (see the format above).  0 when invalid. */
 size_t moe_expert_bytes(int hidden, int inter, int bits, int group);
@@ -114,7 +116,10 @@ size_t moe_expert_bytes(int hidden, int inter, int bits, int group);
  * codes_gate, codes_up, codes_down, sb_gate, sb_up, sb_down. */
 int moe_expert_offsets(int hidden, int inter, int bits, int group, size_t out[6]);
 /* Workspace bytes that moe_layer_decode / moe_route / moe_expert_forward_*
- * need for this layer and token count (0 if the layer is invalid). */
+ * need for this layer and token count (0 if the layer is invalid): the
+ * intermediates that [openclawradar] "Deferred GPU expert compute" keeps on
+ * the device between the routing and the expert pass (logits, gate sigma,
+ * SwiGLU outputs, the shared expert's output). */
 size_t moe_layer_workspace_bytes(const moe_layer_t *L, int n_tokens);
 /* Workspace bytes moe_stack_decode needs for `n_layers` layers shaped like L. */
 size_t moe_stack_workspace_bytes(const moe_layer_t *L, int n_layers);
@@ -131,7 +136,8 @@ size_t moe_stack_workspace_bytes(const moe_layer_t *L, int n_layers);
  *   topk_w       [n_tokens][K] fp32: softmax probabilities of those experts
  *                (renormalised to sum 1 when L->renorm_topk)
  *   shared_sigma [n_tokens] fp32: 1 / (1 + exp(-(g . x)))
- *   logits       [n_tokens][E] fp32, or NULL
+ *   logits       [n_tokens][E] fp32, or NULL (16-byte aligned: the top-K
+ *                kernel reads it with 16-byte loads)
  *   ws           workspace of moe_layer_workspace_bytes(L, n_tokens) bytes */
 int moe_route(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, const void *x,
               int32_t *topk_idx, float *topk_w, float *shared_sigma, float *logits,
@@ -167,7 +173,10 @@ int moe_combine(int hidden, int n_routed, const float *h_res, const float *y,
 /* whole layer, whole stack                                                 */
 /* ---------------------------------------------------------------------- */
 /* One MoE layer for n_tokens tokens with no host round trip: routing, the K
- * routed experts and the shared expert, combine + residual.
+ * routed experts and the shared expert, combine + residual ([openclawradar]
+ * "Pipeline performance": routing (softmax + topK) then the expert forward,
+ * combine and norm of one layer; "Deferred GPU expert compute": the expert
+ * pass is queued on the GPU without a host wait).
  *   x        [n_tokens][H] (x_dtype), the normalised activation
  *   h_res    [n_tokens][H] fp32 residual; h_out [n_tokens][H] fp32 (may not
  *            alias h_res)
@@ -215,7 +224,8 @@ typedef struct moe_tier_s *moe_tier_t;
  *                 caller-owned, 256-byte aligned
  * K <= 8 <= n_slots <= E <= 1024; expert_stride a multiple of 256.  Slots are
  * replaced least recently used first.  The tier object is host bookkeeping
- * (no device memory is allocated); one stream at a time may use a tier. */
+ * (no device or page-locked memory is allocated; the routing is read back
+ * into the object itself); one stream at a time may use a tier. */
 int moe_tier_create(const void *host_records, int n_experts, size_t expert_stride,
                     void *cache, int n_slots, moe_tier_t *out);
 int moe_tier_destroy(moe_tier_t t);
@@ -231,7 +241,12 @@ int moe_tier_assign(moe_tier_t t, const int32_t *ids, int n, int32_t *slots, int
  * gate/up and down + combine on the cached records.  L->experts and
  * L->expert_stride are not used; the layer's router, gate vector and shared
  * expert are.  The outputs (topk_idx holds expert ids, not slots) equal those
- * of moe_layer_decode. */
+ * of moe_layer_decode.
+ * Exceptions to the conventions above, both forced by the host read-back:
+ * the call synchronises `stream` once per token, and a failure found after
+ * the read-back (a routing id outside [0, E), which only NaN logits can
+ * produce) returns MOE_EINVAL with the router and top-K kernels already
+ * enqueued and no expert kernel after them. */
 int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype, const void *x,
                           const float *h_res, float *h_out, int32_t *topk_idx, float *topk_w,
                           void *ws, size_t ws_bytes, void *stream);

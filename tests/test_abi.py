@@ -104,6 +104,9 @@ def test_other_entry_points_validate():
     ws = 0x400000
     assert moe.lib.moe_route(C.byref(L), 1, 1, 0, 0x1000, 0x2000, 0x3000, None, ws, 1 << 20, None) == moe.MOE_EINVAL
     assert moe.lib.moe_route(C.byref(L), 1, 5, 0x500000, 0x1000, 0x2000, 0x3000, None, ws, 1 << 20, None) == moe.MOE_EUNSUPPORTED
+    # caller logits are read with 16-byte loads
+    assert moe.lib.moe_route(C.byref(L), 1, 1, 0x500000, 0x1000, 0x2000, 0x3000, 0x4004, ws, 1 << 20, None) == moe.MOE_EALIGN
+    assert "16-byte" in _err()
     # 2-bit entry point on a 4-bit layer
     assert moe.lib.moe_expert_forward_q2(C.byref(L), 1, 0x500000, 0x1000, 1, 0x2000, None, ws, 1 << 20, None) == moe.MOE_EUNSUPPORTED
     assert moe.lib.moe_expert_forward_q4(C.byref(L), 1, 0x500000, 0x1000, 0, 0x2000, None, ws, 1 << 20, None) == moe.MOE_EINVAL
@@ -137,3 +140,4 @@ def test_gdn_step_validates():
     assert g(1, 64, 128, 128, 0x1004, *ok[1:], None) == moe.MOE_EALIGN
     assert g(1, 64, 128, 128, *ok[:5], 0x6008, 0x7000, None) == moe.MOE_EALIGN
     assert g(1, 64, 128, 128, *ok[:6], 0x7002, None) == moe.MOE_EALIGN
+

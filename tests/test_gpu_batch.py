@@ -63,9 +63,10 @@ def test_tiny_batch(seed):
     log(f"  worst err(out) {err:.2e}")
 
 
-def test_q4_batch16():
+@pytest.mark.parametrize("seed", [4, 5, 6, 7])
+def test_q4_batch16(seed):
     cfg = synth.CONFIGS["q4_batch16"]
-    case = make_batch_case(cfg, 4, target_distinct=40)
-    log(f"q4 batch of 16, seed 4: rho {case.rho:.2f}, {case.distinct} distinct routed experts")
+    case = make_batch_case(cfg, seed, target_distinct=40)
+    log(f"q4 batch of 16, seed {seed}: rho {case.rho:.2f}, {case.distinct} distinct routed experts")
     err = _check(case, *_run(cfg, case))
     log(f"  worst err(out) {err:.2e}")

@@ -73,7 +73,7 @@ def test_tiny_layer_64_seeds():
 @pytest.mark.parametrize("name", ["q4_layer", "q2_layer"])
 def test_qwen_layer(name):
     cfg = synth.CONFIGS[name]
-    for seed, renorm in ((1, True), (2, False), (3, True), (4, True)):
+    for seed, renorm in [(s, r) for s in range(1, 9) for r in (True, False)]:
         log(f"{name} seed={seed} renorm={renorm}")
         case = make_layer_case(cfg, seed, renorm)
         pool, stride = expert_pool(cfg, seed)

@@ -107,3 +107,33 @@ def test_combine():
     torch.cuda.synchronize()
     want = oracle.get().combine(h_res, y, w, ys, float(sig[0]))
     assert err_metric(out.cpu().numpy(), want) <= 1e-5
+
+
+def test_shared_of_another_width_gives_nan_rows_in_bounds():
+    """A 4-bit expert-forward call that lists MOE_SHARED while the layer's
+    shared record is 2-bit: that entry yields NaN rows, and no kernel reads the
+    shared record with the 4-bit geometry (it is held in an allocation of
+    exactly its own size, 3,932,160 bytes, so a read past it would land
+    outside; the routed entries next to it must still be right)."""
+    from bit_dequant_expert_route_amd import moe
+    cfg = synth.CONFIGS["q4_layer"]
+    case = make_layer_case(cfg, 31, True)
+    pool, stride = expert_pool(cfg, 31)
+    sb2 = synth.record_layout(cfg.hidden, cfg.inter, 2).total
+    assert sb2 == 3932160
+    shared2 = torch.empty(sb2, dtype=torch.uint8, device="cuda")
+    moe.fill_experts(shared2, sb2, 1, 31, 0, synth.SHARED_GEN_ID, cfg.hidden, cfg.inter, 2,
+                     synth.dist_for_bits(2))
+    layer = make_layer(cfg, case, pool, stride, shared_dev=shared2, bits_shared=2)
+    e0 = int(case.route["idx"][0])
+    ids_list = [moe.MOE_SHARED, e0, moe.MOE_SHARED]
+    ids = torch.tensor(ids_list, dtype=torch.int32, device="cuda")
+    y = torch.empty(len(ids_list), cfg.hidden, device="cuda")
+    h = torch.empty(len(ids_list), cfg.inter, device="cuda")
+    moe.expert_forward(layer, 4, x_dev(case), ids, y, h)
+    torch.cuda.synchronize()
+    y, h = y.cpu().numpy(), h.cpu().numpy()
+    for j in (0, 2):
+        assert np.all(np.isnan(y[j])) and np.all(np.isnan(h[j]))
+    hh, yy = oracle.get().expert(case.records[e0], cfg.hidden, cfg.inter, 4, case.x64)
+    assert err_metric(h[1], hh) <= TOL and err_metric(y[1], yy) <= TOL
