@@ -649,6 +649,23 @@ int moe_layer_decode(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, cons
                      static_cast<uint8_t *>(ws), wl, s);
 }
 
+int moe_layer_decode_noalloc(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype,
+                             const void *x, const float *h_res, float *h_out,
+                             int32_t *topk_idx, float *topk_w, void *stream) {
+  int st;
+  if ((st = check_decode_args(L, n_tokens, x_dtype, x, h_res, h_out, topk_idx, topk_w)) != MOE_OK)
+    return st;
+  const size_t need = ws_layout(L, n_tokens, 0).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(MOE_EWORKSPACE, "this layer and token count need %zu bytes of workspace; the "
+                "library's own scratch holds %zu (use moe_layer_decode with a workspace)",
+                need, kNoAllocScratchBytes);
+  void *scratch = nullptr;
+  MOE_TRY_HIP(noalloc_scratch(&scratch), "looking up the scratch array");
+  return moe_layer_decode(L, n_tokens, x_dtype, x, h_res, h_out, topk_idx, topk_w, scratch,
+                          kNoAllocScratchBytes, stream);
+}
+
 int moe_layer_ws_view(const moe_layer_t *L, int n_tokens, void *ws, size_t ws_bytes,
                       moe_ws_view *view) {
   int st;

@@ -250,6 +250,11 @@ struct GdnParams {
 };
 hipError_t launch_gdn_step(const GdnParams &p, hipStream_t s);
 
+// workspace of moe_layer_decode_noalloc: a device array of this many bytes
+// per GPU (moe_util.hip); *out receives the current device's address of it
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+hipError_t noalloc_scratch(void **out);
+
 // bytes of the staged-x buffers for a row of `cols` columns at `bits`
 size_t xstage_pair_bytes(int cols, int bits);
 size_t xstage_sum_bytes(int cols, int bits);

@@ -4,9 +4,42 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 namespace moe_impl {
 
 thread_local LaunchEvents g_launch_events;
+
+// ---------------------------------------------------------------------------
+// the workspace of the no-allocation entry point: one array per GPU the
+// library runs on, held until the process ends.  Host code never passes the
+// array's name to a kernel (in host code it is only a stand-in): each device's
+// address is looked up once, with that device current, and kept here.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 
 // ---------------------------------------------------------------------------

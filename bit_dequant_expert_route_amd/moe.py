@@ -67,6 +67,7 @@ def _load():
         "moe_expert_forward_q2": (I, [C.POINTER(LayerStruct), I, P, P, I, P, P, P, Z, P]),
         "moe_combine": (I, [I, I, P, P, P, P, P, P, P]),
         "moe_layer_decode": (I, [C.POINTER(LayerStruct), I, I, P, P, P, P, P, P, Z, P]),
+        "moe_layer_decode_noalloc": (I, [C.POINTER(LayerStruct), I, I, P, P, P, P, P, P]),
         "moe_layer_ws_view": (I, [C.POINTER(LayerStruct), I, P, Z, C.POINTER(WsView)]),
         "moe_stack_decode": (I, [C.POINTER(LayerStruct), I, P, P, P, P, P, Z, P]),
         "moe_graph_capture_begin": (I, [P]),
@@ -214,6 +215,15 @@ def layer_decode(layer: Layer, x, h_res, h_out, topk_idx, topk_w, ws=None, strea
     _check(_lib.moe_layer_decode(C.byref(layer.s), T, _dtype_code(x), _ptr(x), _ptr(h_res),
                                  _ptr(h_out), _ptr(topk_idx), _ptr(topk_w), wp, wb,
                                  _stream(stream)), "moe_layer_decode")
+
+
+def layer_decode_noalloc(layer: Layer, x, h_res, h_out, topk_idx, topk_w, stream=None):
+    """moe_layer_decode with the library's own scratch array as the workspace."""
+    T = x.shape[0] if x.dim() == 2 else 1
+    _check(_lib.moe_layer_decode_noalloc(C.byref(layer.s), T, _dtype_code(x), _ptr(x),
+                                         _ptr(h_res), _ptr(h_out), _ptr(topk_idx),
+                                         _ptr(topk_w), _stream(stream)),
+           "moe_layer_decode_noalloc")
 
 
 def ws_view(layer: Layer, n_tokens: int, ws) -> dict:

@@ -187,6 +187,24 @@ int moe_layer_decode(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype, cons
                      const float *h_res, float *h_out, int32_t *topk_idx, float *topk_w,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_layer_decode with its workspace in a library-owned device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU instead of a caller's buffer.  The call
+ * allocates nothing.  The array lives until the process ends; the first call
+ * on a device looks up its address there (make that first call outside a
+ * graph capture).  A layer and token count whose workspace
+ * (moe_layer_workspace_bytes) exceeds the array are refused with
+ * MOE_EWORKSPACE before anything is enqueued; the q4 layer needs about 0.3
+ * MiB for one token and 1.7 MiB for 16.  Every call on one GPU shares its
+ * array and leaves its intermediates there (nothing in it has to start at
+ * zero): calls that overlap in time on one GPU, on different streams or
+ * from different threads, race. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_layer_decode_noalloc(const moe_layer_t *L, int n_tokens, moe_dtype x_dtype,
+                             const void *x, const float *h_res, float *h_out,
+                             int32_t *topk_idx, float *topk_w, void *stream);
+
 /* Device pointers of the intermediates moe_layer_decode leaves in ws. */
 typedef struct moe_ws_view {
     float *logits;       /* [n_tokens][E] */

@@ -141,3 +141,19 @@ def test_gdn_step_validates():
     assert g(1, 64, 128, 128, *ok[:5], 0x6008, 0x7000, None) == moe.MOE_EALIGN
     assert g(1, 64, 128, 128, *ok[:6], 0x7002, None) == moe.MOE_EALIGN
 
+
+def test_noalloc_refuses_a_workspace_beyond_its_scratch():
+    """The largest shapes need more workspace than the library's scratch array
+    holds: refused with MOE_EWORKSPACE before anything is enqueued (no GPU
+    call is made on this path)."""
+    L = _layer(hidden=8192, inter=8192, top_k=8, n_experts=1024, expert_stride=moe.expert_bytes(8192, 8192, 4))
+    need = moe.lib.moe_layer_workspace_bytes(C.byref(L), 64)
+    assert need > (8 << 20)
+    st = moe.lib.moe_layer_decode_noalloc(C.byref(L), 64, 1, 0x500000, 0x600000, 0x700000,
+                                          0x800000, 0x900000, None)
+    assert st == moe.MOE_EWORKSPACE
+    assert "scratch" in _err()
+    # and invalid layers are refused first
+    st = moe.lib.moe_layer_decode_noalloc(C.byref(_layer(group=32)), 1, 1, 0x500000, 0x600000,
+                                          0x700000, 0x800000, 0x900000, None)
+    assert st == moe.MOE_EUNSUPPORTED
