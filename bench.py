@@ -48,6 +48,10 @@ def parse():
                     help="q4_tier: AR(1) coefficient of consecutive tokens' activations")
     ap.add_argument("--tier-tokens", type=int, default=256, help="q4_tier: timed tokens")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="q4_layer: skip the 60-layer stack figure reported beside the layer")
+    ap.add_argument("--stack-steps", type=int, default=10,
+                    help="q4_layer: timed tokens of the 60-layer stack figure")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-passes", type=int, default=3)
     ap.add_argument("--copy-probe", action="store_true",
@@ -259,6 +263,42 @@ def bench_stack(cfg, args):
     rec = moe.profile_end(n_launch)
     graph.destroy()
     return ms, rec, dict(layers=L, distinct=None)
+
+
+def stack_figure(args):
+    """The 60-layer resident stack (217 GB of experts, one token through every
+    layer, graph-replayed) measured in the same run as the layer: per-token
+    latency, per layer, and its effective HBM rate over the layers' bytes."""
+    import gc
+    import torch
+    from bit_dequant_expert_route_amd import synth
+    gc.collect()
+    torch.cuda.empty_cache()
+    cfg = synth.CONFIGS["q4_stack"]
+    sargs = argparse.Namespace(**vars(args))
+    sargs.steps, sargs.warmup, sargs.profile_passes = args.stack_steps, 2, 1
+    t0 = time.perf_counter()
+    ms_token, rec, _ = bench_stack(cfg, sargs)
+    wall = time.perf_counter() - t0
+    per = {}
+    for name, ms in rec:
+        per.setdefault(name, []).append(ms)
+    lb = kernel_bytes(cfg)["layer_total"] * cfg.n_layers
+    gbps = lb / (ms_token * 1e-3) / 1e9
+    out = {"workload": f"q4_stack: {cfg.n_layers} layers of the q4 layer shape, each with its own "
+                       f"512 experts (217 GB resident), one token, h += u_l and RMSNorm between "
+                       f"layers, one HIP graph per token",
+           "us_per_token": round(ms_token * 1000.0, 2),
+           "us_per_layer": round(ms_token * 1000.0 / cfg.n_layers, 3),
+           "tokens_per_s": round(1000.0 / ms_token, 2),
+           "hbm_bytes_per_token": lb, "effective_GBps": round(gbps, 1),
+           "pct_hbm_peak": round(100.0 * gbps / PEAK_GBPS, 2),
+           "steps": sargs.steps, "warmup": sargs.warmup,
+           "kernels_us": {k: round(float(np.mean(v) * 1000.0), 3) for k, v in per.items()},
+           "leg_wall_s": round(wall, 1)}
+    gc.collect()
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_batch(cfg, args):
@@ -701,6 +741,8 @@ def main():
     valu = valu_from_profiles(args.workload, dom, kern_us[dom])
     if valu:
         line["valu_issue"] = {"kernel": dom_kernel, **valu}
+    if args.workload == "q4_layer" and not args.no_stack:
+        line["stack_60_layers"] = stack_figure(args)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -158,7 +158,7 @@ struct GateUpParams {
   const void *x;                  // [H]
   float *h_out;                   // [n][I]
   // the shared expert's gate/up in the same launch (same width): its
-  // workgroups come first and need no routing
+  // workgroups come after the routed ones and need no routing
   int with_shared;
   float *h_shared_out;            // [I]
   int n_shared_blocks;            // set by the launcher

@@ -138,11 +138,14 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
   static_assert(kBlock / 64 == 4, "the selection is split over four waves");
   const int blk = wave_uniform(blockIdx.x);
   const int wv = wave_uniform(threadIdx.x >> 6);
-  const bool shared_blk = blk < p.n_shared_blocks;
-  // the shared expert does not depend on the routing: its workgroups come
-  // first and stream its rows while the routed ones are selecting experts
-  const int wave = shared_blk ? blk * (kBlock / 64) + wv
-                              : (blk - p.n_shared_blocks) * (kBlock / 64) + wv;
+  // The routed workgroups come first in the grid, so they are dispatched and
+  // issue their logit loads ahead of the shared expert's: those need no
+  // routing and stream the shared rows while the routed ones select experts
+  // (q4 layer 20.36 -> 20.10 us per layer with this order)
+  const int n_routed_blocks = (int)gridDim.x - p.n_shared_blocks;
+  const bool shared_blk = blk >= n_routed_blocks;
+  const int wave = shared_blk ? (blk - n_routed_blocks) * (kBlock / 64) + wv
+                              : blk * (kBlock / 64) + wv;
   const int slot = shared_blk ? 0 : wave / p.waves_per_expert;
   const int wie = shared_blk ? wave : wave - slot * p.waves_per_expert;
   const bool topk = !shared_blk && !p.ids;  // workgroup-uniform
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
   gu_load(tile, rec, from_shared ? p.soff : p.off, m, p.I, row0);
   __builtin_amdgcn_sched_barrier(0);
   // the first routed workgroup also reports the selection and its weights
-  if (topk && blk == p.n_shared_blocks && wv == 0)
+  if (topk && blk == 0 && wv == 0)
     topk_store(sel_e, topk_merge_weight(tsh, p.K, p.renorm, sel_e, sel_key, top_key), p.K,
                p.idx_out, p.w_out);
 #pragma unroll
@@ -224,11 +227,14 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
   constexpr bool XF32 = XS != XS_BF16;
   const int blk = wave_uniform(blockIdx.x);
   const int wv = wave_uniform(threadIdx.x >> 6);
-  const bool shared_blk = blk < p.n_shared_blocks;
-  // the shared expert does not depend on the routing: its workgroups come
-  // first and stream its rows while the routed ones are selecting experts
-  const int wave = shared_blk ? blk * (kBlock / 64) + wv
-                              : (blk - p.n_shared_blocks) * (kBlock / 64) + wv;
+  // The routed workgroups come first in the grid, so they are dispatched and
+  // issue their logit loads ahead of the shared expert's: those need no
+  // routing and stream the shared rows while the routed ones select experts
+  // (q4 layer 20.36 -> 20.10 us per layer with this order)
+  const int n_routed_blocks = (int)gridDim.x - p.n_shared_blocks;
+  const bool shared_blk = blk >= n_routed_blocks;
+  const int wave = shared_blk ? (blk - n_routed_blocks) * (kBlock / 64) + wv
+                              : blk * (kBlock / 64) + wv;
   const int slot = shared_blk ? 0 : wave / p.waves_per_expert;
   const int wie = shared_blk ? wave : wave - slot * p.waves_per_expert;
   const bool topk = !shared_blk && !p.ids;  // workgroup-uniform
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
   }
   __builtin_amdgcn_sched_barrier(0);
   // the first routed workgroup also reports the selection and its weights
-  if (topk && blk == p.n_shared_blocks && wv == 0)
+  if (topk && blk == 0 && wv == 0)
     topk_store(sel_e, topk_merge_weight(tsh, p.K, p.renorm, sel_e, sel_key, top_key), p.K,
                p.idx_out, p.w_out);
   XStage<BITS, XF32> xs[NCH];
