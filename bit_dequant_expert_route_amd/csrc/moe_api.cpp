@@ -15,7 +15,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <mutex>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -81,7 +80,7 @@ bool dim_ok(int d) { return d >= 64 && d <= kMaxDim && d % kGroup == 0; }
 // ---------------------------------------------------------------------------
 struct WsLayout {
   size_t logits, sigma, h_routed, h_shared, y_shared, x_stage, hres_stage, xs_pairs, xs_sums,
-      h_pong, y_routed, g_count, g_expert, g_start, g_pair, ids, total;
+      h_pong, y_routed, g_count, g_expert, g_start, g_pair, ids, rec_src, total;
   size_t xs_pair_stride, xs_sum_stride;  // per token, in u32 / floats
 };
 
@@ -112,6 +111,7 @@ WsLayout ws_layout(const moe_layer_t *L, int T, int n_layers) {
   w.g_start = o; o += batch ? up256(4 * (P + 2)) : 0;
   w.g_pair = o; o += batch ? up256(4 * P) : 0;
   w.ids = o; o += up256(4 * (size_t)kMaxK);  // cache slots of the routed experts (tier path)
+  w.rec_src = o; o += up256(16 * (size_t)kMaxK);  // their record addresses and fill targets (tier)
   w.total = o;
   return w;
 }
@@ -723,40 +723,50 @@ int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *up
 }
 
 // ---------------------------------------------------------------------------
-// host-memory expert tier
+// host-memory expert tier: the routed records in page-locked host memory, a
+// cache of n_slots records and the slot table in device memory, all managed
+// on the device (no host round trip, so a token's calls can be captured)
 // ---------------------------------------------------------------------------
 struct moe_tier_s {
-  const uint8_t *host;
+  const uint8_t *host;       // as given
+  const uint8_t *host_dev;   // its device address
   int E;
   size_t stride;
   uint8_t *cache;
   int n_slots;
-  std::vector<int32_t> slot_of;  // expert -> slot, or -1
-  std::vector<int32_t> owner;    // slot -> expert, or -1
-  std::vector<uint64_t> used;    // slot -> tick of its last use (0: never)
-  uint64_t tick = 0, hits = 0, misses = 0, bytes = 0;
-  int32_t routing[2 * kMaxK];    // the routed ids read back, then their slots
-  std::mutex mu;
+  uint8_t *state;
 };
 
+size_t moe_tier_state_bytes(int n_experts, int n_slots) {
+  if (n_experts < 1 || n_experts > kMaxE || n_slots < kMaxK || n_slots > n_experts) return 0;
+  return up256(kTierOwnerOff + (size_t)n_slots * 8);
+}
+
 int moe_tier_create(const void *host_records, int n_experts, size_t expert_stride, void *cache,
-                    int n_slots, moe_tier_t *out) {
+                    int n_slots, void *state, moe_tier_t *out) {
   if (!out) return fail(MOE_EINVAL, "out is NULL");
-  if (!host_records || !cache) return fail(MOE_EINVAL, "host_records / cache is NULL");
+  if (!host_records || !cache || !state) return fail(MOE_EINVAL, "host_records / cache / state is NULL");
   if (n_experts < 1 || n_experts > kMaxE) return fail(MOE_EINVAL, "n_experts = %d: need 1..1024", n_experts);
   if (n_slots < kMaxK || n_slots > n_experts)
     return fail(MOE_EINVAL, "n_slots = %d: need 8..n_experts", n_slots);
-  if (expert_stride == 0 || expert_stride % 256 || !aligned(cache, 256))
-    return fail(MOE_EALIGN, "cache and expert_stride must be 256-byte aligned");
+  if (expert_stride == 0 || expert_stride % 256 || !aligned(cache, 256) || !aligned(state, 256) ||
+      !aligned(host_records, 256))
+    return fail(MOE_EALIGN, "host_records, cache, state and expert_stride must be 256-byte aligned");
+  // the kernels read missing records from host memory through its device
+  // address: only page-locked memory the device can map has one
+  void *dev = nullptr;
+  const hipError_t e = hipHostGetDevicePointer(&dev, const_cast<void *>(host_records), 0);
+  if (e != hipSuccess || !dev)
+    return fail(MOE_EINVAL, "host_records must be page-locked host memory the device can read "
+                "(hipHostMalloc): %s", hipGetErrorString(e));
   moe_tier_s *t = new moe_tier_s;
   t->host = static_cast<const uint8_t *>(host_records);
+  t->host_dev = static_cast<const uint8_t *>(dev);
   t->E = n_experts;
   t->stride = expert_stride;
   t->cache = static_cast<uint8_t *>(cache);
   t->n_slots = n_slots;
-  t->slot_of.assign(n_experts, -1);
-  t->owner.assign(n_slots, -1);
-  t->used.assign(n_slots, 0);
+  t->state = static_cast<uint8_t *>(state);
   *out = t;
   return MOE_OK;
 }
@@ -767,44 +777,25 @@ int moe_tier_destroy(moe_tier_t t) {
   return MOE_OK;
 }
 
-int moe_tier_assign(moe_tier_t t, const int32_t *ids, int n, int32_t *slots, int32_t *miss) {
-  if (!t || !ids || !slots) return fail(MOE_EINVAL, "tier / ids / slots is NULL");
-  if (n < 0 || n > t->n_slots) return fail(MOE_EINVAL, "n = %d: need 0..n_slots", n);
-  for (int i = 0; i < n; ++i)
-    if (ids[i] < 0 || ids[i] >= t->E) return fail(MOE_EINVAL, "expert id %d out of range", ids[i]);
-  std::lock_guard<std::mutex> lk(t->mu);
-  const uint64_t now = ++t->tick;
-  for (int i = 0; i < n; ++i) {
-    const int e = ids[i];
-    int s = t->slot_of[e];
-    const bool hit = s >= 0;
-    if (hit) {
-      ++t->hits;
-    } else {
-      // least recently used slot not taken by this call (never-used slots
-      // have tick 0 and go first); n <= n_slots leaves one
-      s = -1;
-      for (int j = 0; j < t->n_slots; ++j)
-        if (t->used[j] < now && (s < 0 || t->used[j] < t->used[s])) s = j;
-      if (t->owner[s] >= 0) t->slot_of[t->owner[s]] = -1;
-      t->owner[s] = e;
-      t->slot_of[e] = s;
-      ++t->misses;
-    }
-    t->used[s] = now;
-    slots[i] = s;
-    if (miss) miss[i] = hit ? 0 : 1;
-  }
+int moe_tier_reset(moe_tier_t t, void *stream) {
+  if (!t) return fail(MOE_EINVAL, "tier is NULL");
+  MOE_TRY_HIP(launch_tier_reset(t->state, t->n_slots, static_cast<hipStream_t>(stream)), "tier reset launch");
   return MOE_OK;
 }
 
-int moe_tier_stats(moe_tier_t t, unsigned long long *hits, unsigned long long *misses,
-                   unsigned long long *bytes_copied) {
+int moe_tier_stats(moe_tier_t t, void *stream, unsigned long long *hits, unsigned long long *misses,
+                   unsigned long long *bytes_read, int32_t *slot_owner) {
   if (!t) return fail(MOE_EINVAL, "tier is NULL");
-  std::lock_guard<std::mutex> lk(t->mu);
-  if (hits) *hits = t->hits;
-  if (misses) *misses = t->misses;
-  if (bytes_copied) *bytes_copied = t->bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TierState st;
+  MOE_TRY_HIP(hipMemcpyAsync(&st, t->state, sizeof st, hipMemcpyDeviceToHost, s), "tier state copy");
+  if (slot_owner)
+    MOE_TRY_HIP(hipMemcpyAsync(slot_owner, t->state + kTierOwnerOff, sizeof(int32_t) * t->n_slots,
+                               hipMemcpyDeviceToHost, s), "tier slot copy");
+  MOE_TRY_HIP(hipStreamSynchronize(s), "waiting for the tier state");
+  if (hits) *hits = st.hits;
+  if (misses) *misses = st.misses;
+  if (bytes_read) *bytes_read = st.bytes;
   return MOE_OK;
 }
 
@@ -813,7 +804,7 @@ int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype,
                           void *ws, size_t ws_bytes, void *stream) {
   if (!L) return fail(MOE_EINVAL, "layer is NULL");
   if (!t) return fail(MOE_EINVAL, "tier is NULL");
-  moe_layer_t Lc = *L;  // the routed records come from the tier's cache
+  moe_layer_t Lc = *L;  // the routed records come from the tier
   Lc.experts = t->cache;
   Lc.expert_stride = t->stride;
   int st;
@@ -822,6 +813,7 @@ int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype,
     return fail(MOE_EINVAL, "the tier holds %d experts, the layer has %d", t->E, L->n_experts);
   const size_t rb = moe_expert_bytes(L->hidden, L->inter, L->bits_routed, L->group);
   if (t->stride < rb) return fail(MOE_EINVAL, "tier stride %zu < record size %zu", t->stride, rb);
+  if (L->top_k > t->n_slots) return fail(MOE_EINVAL, "top_k %d > tier slots %d", L->top_k, t->n_slots);
   if ((st = check_dtype(x_dtype, "x_dtype")) != MOE_OK) return st;
   if ((st = check_vec(x, "x")) != MOE_OK) return st;
   if ((st = check_vec(h_res, "h_res")) != MOE_OK) return st;
@@ -832,10 +824,6 @@ int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype,
   const WsLayout wl = ws_layout(L, 1, 0);
   if ((st = check_ws(ws, ws_bytes, wl.total)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  MOE_TRY_HIP(hipStreamIsCapturing(s, &cs), "hipStreamIsCapturing");
-  if (cs != hipStreamCaptureStatusNone)
-    return fail(MOE_EINVAL, "the tier path waits for the routing on the host and cannot be captured");
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   float *logits = reinterpret_cast<float *>(wsb + wl.logits);
   float *sigma = reinterpret_cast<float *>(wsb + wl.sigma);
@@ -843,11 +831,13 @@ int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype,
   float *h_shared = reinterpret_cast<float *>(wsb + wl.h_shared);
   float *y_shared = reinterpret_cast<float *>(wsb + wl.y_shared);
   int32_t *slot_ids = reinterpret_cast<int32_t *>(wsb + wl.ids);
+  uint64_t *rec_src = reinterpret_cast<uint64_t *>(wsb + wl.rec_src);
+  uint64_t *rec_fill = rec_src + kMaxK;
   const int K = L->top_k;
   const int xsrc = x_dtype == MOE_BF16 ? XS_BF16 : XS_F32;
   const bool same = L->bits_shared == L->bits_routed;
 
-  // router rows, shared gate (and the shared gate/up at another width), top-K
+  // router rows, shared gate (and the shared gate/up at another width)
   HeadParams hp = head_params(&Lc, 1);
   hp.xsrc = xsrc;
   hp.x = x;
@@ -857,34 +847,27 @@ int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype,
   hp.n_shared_waves = same ? 0 : 1;
   hp.bits_routed = L->bits_routed;
   MOE_TRY_HIP(timed(s, MOE_KERNEL_HEAD, [&] { return launch_head(hp, s); }), "router launch");
-  TopkParams tp;
+  // top-K and the slot of every selected expert, on the device
+  TierRouteParams tp;
   tp.logits = logits;
-  tp.T = 1;
   tp.E = L->n_experts;
   tp.K = K;
   tp.renorm = L->renorm_topk;
+  tp.n_slots = t->n_slots;
+  tp.state = t->state;
+  tp.host_dev = t->host_dev;
+  tp.cache = t->cache;
+  tp.stride = t->stride;
+  tp.record_bytes = rb;
   tp.idx = topk_idx;
   tp.w = topk_w;
-  MOE_TRY_HIP(timed(s, MOE_KERNEL_TOPK, [&] { return launch_topk(tp, s); }), "top-K launch");
+  tp.slot = slot_ids;
+  tp.rec_src = rec_src;
+  tp.rec_fill = rec_fill;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_TOPK, [&] { return launch_tier_route(tp, s); }), "tier routing launch");
 
-  // the routing on the host (read back into the tier object), then the
-  // missing records into their slots
-  int32_t *ids = t->routing, *slots = t->routing + kMaxK;
-  int32_t miss[kMaxK];
-  MOE_TRY_HIP(hipMemcpyAsync(ids, topk_idx, K * sizeof(int32_t), hipMemcpyDeviceToHost, s), "routing copy");
-  MOE_TRY_HIP(hipStreamSynchronize(s), "waiting for the routing");
-  if ((st = moe_tier_assign(t, ids, K, slots, miss)) != MOE_OK) return st;
-  for (int k = 0; k < K; ++k) {
-    if (!miss[k]) continue;
-    MOE_TRY_HIP(hipMemcpyAsync(t->cache + (size_t)slots[k] * t->stride, t->host + (size_t)ids[k] * t->stride,
-                               rb, hipMemcpyHostToDevice, s),
-                "expert record copy");
-    std::lock_guard<std::mutex> lk(t->mu);
-    t->bytes += rb;
-  }
-  MOE_TRY_HIP(hipMemcpyAsync(slot_ids, slots, K * sizeof(int32_t), hipMemcpyHostToDevice, s), "slot copy");
-
-  // gate/up of the cached records (+ the shared expert), down + combine
+  // gate/up of the slots' records (hits from the cache, misses from host
+  // memory, written into their slots) + the shared expert, down + combine
   GateUpParams gp;
   memset(&gp, 0, sizeof gp);
   gp.H = L->hidden;
@@ -905,6 +888,8 @@ int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype,
   gp.h_out = h_routed;
   gp.with_shared = same;
   gp.h_shared_out = h_shared;
+  gp.rec_src = rec_src;
+  gp.rec_fill = rec_fill;
   MOE_TRY_HIP(timed(s, MOE_KERNEL_GATEUP, [&] { return launch_gateup(gp, s); }), "gate/up launch");
   DownParams dp;
   memset(&dp, 0, sizeof dp);
@@ -939,6 +924,8 @@ int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype,
   dp.y = same ? nullptr : y_shared;
   dp.h_res = h_res;
   dp.out = h_out;
+  // the gate/up launch has filled every missing record's slot, down rows
+  // included: the down kernel reads all routed records from their slots
   MOE_TRY_HIP(timed(s, MOE_KERNEL_DOWN, [&] { return launch_down(dp, s); }), "down/combine launch");
   return MOE_OK;
 }

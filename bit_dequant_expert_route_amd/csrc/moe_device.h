@@ -557,6 +557,34 @@ __device__ __forceinline__ void gu_load(GUTile<BITS, NCH, NPASS> &t, const uint8
   }
 }
 
+// the same words written back at the same offsets of another record (the
+// expert tier's read-through fill of a cache slot; positions past the end
+// rewrite row 0 / chunk 0 with what they read there)
+template <int BITS, int NCH, int NPASS>
+__device__ __forceinline__ void gu_store(const GUTile<BITS, NCH, NPASS> &t, uint8_t *rec,
+                                         const RecOffsets &off, const RowMap &m, int I, int row0) {
+  uint32_t *gc = reinterpret_cast<uint32_t *>(rec + off.gate_codes);
+  uint32_t *uc = reinterpret_cast<uint32_t *>(rec + off.up_codes);
+  uint32_t *gs = reinterpret_cast<uint32_t *>(rec + off.gate_sb);
+  uint32_t *us = reinterpret_cast<uint32_t *>(rec + off.up_sb);
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const int r = row0 + p * m.rpp + m.rip;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = m.li + (j << m.lg);
+      const bool in = r < I && c < m.cpr;
+      const int rr = in ? r : 0, cc = in ? c : 0;
+      const size_t wo = (size_t)rr * m.wpr + (size_t)cc * 4;
+      const size_t so = (size_t)rr * m.gpr + chunk_group<BITS>(cc);
+      *reinterpret_cast<uint4 *>(gc + wo) = t.gq[p][j];
+      *reinterpret_cast<uint4 *>(uc + wo) = t.uq[p][j];
+      gs[so] = t.gs[p][j];
+      us[so] = t.us[p][j];
+    }
+  }
+}
+
 __device__ __forceinline__ bool in_tile(const RowMap &m, int rows, int row0, int p, int j) {
   return row0 + p * m.rpp + m.rip < rows && m.li + (j << m.lg) < m.cpr;
 }
@@ -1206,6 +1234,13 @@ __device__ __forceinline__ void down_load(DnTile<BITS, NCH, NPASS> &t, const uin
       t.sb[p][j] = ds[(size_t)rr * m.gpr + chunk_group<BITS>(cc)];
     }
   }
+}
+
+// a 64-bit pointer the wave holds in every lane, made wave-uniform
+__device__ __forceinline__ uint64_t wave_uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // weighted partial sums of one expert into acc[p]; the passes are taken in

@@ -164,6 +164,14 @@ struct GateUpParams {
   int n_shared_blocks;            // set by the launcher
   int rows_per_wave;
   int waves_per_expert;
+  // expert tier: per list entry, the address of the record to read (a cache
+  // slot, or the record in host memory on a miss) and where to write the
+  // rows read (the slot on a miss, else 0); null outside the tier path
+  const uint64_t *rec_src;        // [n]
+  const uint64_t *rec_fill;       // [n]
+  // with rec_fill: workgroups after all others copy the down section of every
+  // entry that has a fill target (set by the launcher)
+  int n_copy_blocks, copy_blocks_per_entry;
 };
 hipError_t launch_gateup(const GateUpParams &p, hipStream_t s);
 
@@ -200,6 +208,34 @@ struct DownParams {
   int waves_per_expert;           // Y mode
 };
 hipError_t launch_down(const DownParams &p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// expert tier: top-K of one token's logits, then each selected expert's cache
+// slot from the device-resident state (least recently used slot not taken by
+// this token on a miss), and the record address every expert kernel reads
+// ---------------------------------------------------------------------------
+struct TierState {                // device layout of the tier state
+  uint32_t tick, pad[1];
+  unsigned long long hits, misses, bytes;
+  // followed at kTierOwnerOff by owner[n_slots] int32 (expert in the slot or
+  // -1), then last_use[n_slots] uint32 (tick of its last use, 0 = never)
+};
+constexpr size_t kTierOwnerOff = 64;
+struct TierRouteParams {
+  const float *logits;            // [E]
+  int E, K, renorm, n_slots;
+  uint8_t *state;
+  const uint8_t *host_dev;        // device address of the host records
+  uint8_t *cache;
+  size_t stride, record_bytes;
+  int32_t *idx;                   // [K] expert ids
+  float *w;                       // [K]
+  int32_t *slot;                  // [K] slot, or -1 for an invalid selection
+  uint64_t *rec_src;              // [K]
+  uint64_t *rec_fill;             // [K]
+};
+hipError_t launch_tier_route(const TierRouteParams &p, hipStream_t s);
+hipError_t launch_tier_reset(uint8_t *state, int n_slots, hipStream_t s);
 
 struct CombineParams {
   int H, K;

@@ -131,6 +131,41 @@ __global__ __launch_bounds__(64) void k_topk(TopkParams p) {
 // K2: gate/up for a list of experts (explicit ids, or the top-K of the
 // logits, computed by every workgroup)
 // ---------------------------------------------------------------------------
+// Expert tier: copy workgroup c moves its share of the down section (codes,
+// then scale/bias words) of entry c / copy_blocks_per_entry from the record it
+// is read from (host memory on a miss) into the entry's cache slot, so that
+// the down kernel reads every record from device memory and the host link
+// carries a missing record's down rows while its gate/up rows stream in.
+constexpr int kCopyUnroll = 8;  // 16-byte words per thread in flight
+
+__device__ __forceinline__ void copy_down_part(const GateUpParams &p, int c) {
+  const int k = c / p.copy_blocks_per_entry;
+  const int part = c - k * p.copy_blocks_per_entry;
+  const uint64_t fill = wave_uniform_u64(p.rec_fill[k]);
+  if (!fill) return;  // a hit: the slot already holds the record
+  const uint8_t *src = reinterpret_cast<const uint8_t *>(wave_uniform_u64(p.rec_src[k]));
+  uint8_t *dst = reinterpret_cast<uint8_t *>(fill);
+  const size_t n_codes = (size_t)p.H * p.I * p.bits / 8 / 16;  // 16-byte words
+  const size_t n_sb = (size_t)p.H * (p.I / kGroup) * 4 / 16;
+  const size_t n = n_codes + n_sb;
+  const size_t per = (n + p.copy_blocks_per_entry - 1) / p.copy_blocks_per_entry;
+  const size_t w0 = (size_t)part * per, w1 = w0 + per < n ? w0 + per : n;
+  for (size_t b = w0 + threadIdx.x; b < w1; b += (size_t)kBlock * kCopyUnroll) {
+    uint4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const size_t i = b + (size_t)u * kBlock;
+      const size_t off = i < n_codes ? p.off.down_codes + i * 16 : p.off.down_sb + (i - n_codes) * 16;
+      if (i < w1) v[u] = *reinterpret_cast<const uint4 *>(src + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const size_t i = b + (size_t)u * kBlock;
+      const size_t off = i < n_codes ? p.off.down_codes + i * 16 : p.off.down_sb + (i - n_codes) * 16;
+      if (i < w1) *reinterpret_cast<uint4 *>(dst + off) = v[u];
+    }
+  }
+}
 template <int BITS, int NCH, int NPASS, int XS>
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
   // each wave stages its own chunks of x (see gateup_x_in_lds)
@@ -142,7 +177,11 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
   // issue their logit loads ahead of the shared expert's: those need no
   // routing and stream the shared rows while the routed ones select experts
   // (q4 layer 20.36 -> 20.10 us per layer with this order)
-  const int n_routed_blocks = (int)gridDim.x - p.n_shared_blocks;
+  const int n_routed_blocks = (int)gridDim.x - p.n_shared_blocks - p.n_copy_blocks;
+  if (blk >= n_routed_blocks + p.n_shared_blocks) {  // workgroup-uniform: a tier copy
+    copy_down_part(p, blk - n_routed_blocks - p.n_shared_blocks);
+    return;
+  }
   const bool shared_blk = blk >= n_routed_blocks;
   const int wave = shared_blk ? (blk - n_routed_blocks) * (kBlock / 64) + wv
                               : blk * (kBlock / 64) + wv;
@@ -204,9 +243,15 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
   const bool valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
   const bool from_shared = shared && valid;
   const uint8_t *rec = from_shared ? p.shared_rec : p.experts + (size_t)(valid && !shared ? id : 0) * p.stride;
+  uint8_t *fill = nullptr;
+  if (p.rec_src && !shared_blk && valid && !shared) {  // the tier's record of this entry
+    rec = reinterpret_cast<const uint8_t *>(wave_uniform_u64(p.rec_src[slot]));
+    fill = reinterpret_cast<uint8_t *>(wave_uniform_u64(p.rec_fill[slot]));
+  }
   GUTile<BITS, NCH, NPASS> tile;
   gu_load(tile, rec, from_shared ? p.soff : p.off, m, p.I, row0);
   __builtin_amdgcn_sched_barrier(0);
+  if (fill) gu_store(tile, fill, p.off, m, p.I, row0);
   // the first routed workgroup also reports the selection and its weights
   if (topk && blk == 0 && wv == 0)
     topk_store(sel_e, topk_merge_weight(tsh, p.K, p.renorm, sel_e, sel_key, top_key), p.K,
@@ -231,7 +276,11 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
   // issue their logit loads ahead of the shared expert's: those need no
   // routing and stream the shared rows while the routed ones select experts
   // (q4 layer 20.36 -> 20.10 us per layer with this order)
-  const int n_routed_blocks = (int)gridDim.x - p.n_shared_blocks;
+  const int n_routed_blocks = (int)gridDim.x - p.n_shared_blocks - p.n_copy_blocks;
+  if (blk >= n_routed_blocks + p.n_shared_blocks) {  // workgroup-uniform: a tier copy
+    copy_down_part(p, blk - n_routed_blocks - p.n_shared_blocks);
+    return;
+  }
   const bool shared_blk = blk >= n_routed_blocks;
   const int wave = shared_blk ? (blk - n_routed_blocks) * (kBlock / 64) + wv
                               : blk * (kBlock / 64) + wv;
@@ -258,12 +307,17 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
   bool valid = false;
   // a list entry may name the shared expert: it still writes its own slot
   float *const hout = shared_blk ? p.h_shared_out : p.h_out + (size_t)slot * p.I;
+  uint8_t *fill = nullptr;
   auto issue = [&](int id) {
     // unreadable entries (see k_gateup) read routed record 0 and yield NaN
     const bool shared = id == kSharedId;
     valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
     const bool from_shared = shared && valid;
     const uint8_t *rec = from_shared ? p.shared_rec : p.experts + (size_t)(valid && !shared ? id : 0) * p.stride;
+    if (p.rec_src && !shared_blk && valid && !shared) {  // the tier's record of this entry
+      rec = reinterpret_cast<const uint8_t *>(wave_uniform_u64(p.rec_src[slot]));
+      fill = reinterpret_cast<uint8_t *>(wave_uniform_u64(p.rec_fill[slot]));
+    }
     gu_load(tile, rec, from_shared ? p.soff : p.off, m, p.I, row0);
   };
   if (!topk && active) issue(shared_blk ? kSharedId : wave_uniform(p.ids[slot]));
@@ -290,6 +344,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
   if (topk && blk == 0 && wv == 0)
     topk_store(sel_e, topk_merge_weight(tsh, p.K, p.renorm, sel_e, sel_key, top_key), p.K,
                p.idx_out, p.w_out);
+  if (fill) gu_store(tile, fill, p.off, m, p.I, row0);
   XStage<BITS, XF32> xs[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
@@ -467,6 +522,109 @@ __global__ __launch_bounds__(kBlock) void k_down_y(DownParams p) {
     const float s = seg_sum(acc[i], m.lg);
     const int r = row0 + i * m.rpp + m.rip;
     if (m.li == 0 && r < p.H) p.y[(size_t)slot * p.H + r] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// expert tier: one wave takes the top-K of the token's logits, then gives
+// each selected expert its cache slot.  The slot table (owner and last use
+// of every slot) is copied to LDS, updated there expert by expert in the
+// order of the selection, and the slots this token used are written back.
+// A hit reads its slot; a miss takes the least recently used slot this token
+// has not used (never-used slots first, the lowest index among equal uses),
+// and the expert kernels read its record from host memory and write it into
+// the slot as they go.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+__global__ __launch_bounds__(64) void k_tier_route(TierRouteParams p) {
+  __shared__ int32_t own[kMaxE];
+  __shared__ uint32_t used[kMaxE];
+  const int lane = lane_id();
+  TierState *st = reinterpret_cast<TierState *>(p.state);
+  int32_t *g_own = reinterpret_cast<int32_t *>(p.state + kTierOwnerOff);
+  uint32_t *g_used = reinterpret_cast<uint32_t *>(g_own + p.n_slots);
+  for (int j = lane; j < p.n_slots; j += 64) {
+    own[j] = g_own[j];
+    used[j] = g_used[j];
+  }
+  const uint32_t tick = st->tick + 1u;
+  float v[kTopkNpl];
+  topk_load(p.logits, p.E, v);
+  int e;
+  float w;
+  topk_select(v, p.E, p.K, p.renorm, e, w);
+  topk_store(e, w, p.K, p.idx, p.w);
+  __syncthreads();
+  int my_slot = -1, my_miss = 0;
+#pragma unroll 1
+  for (int k = 0; k < p.K; ++k) {
+    const int ek = __builtin_amdgcn_readlane(e, k);
+    int s = -1, miss = 0;
+    if (ek >= 0) {  // uniform; a NaN logit can leave a selection empty
+      int found = -1;
+      for (int j = lane; j < p.n_slots; j += 64)
+        if (own[j] == ek) found = j;
+      const uint64_t b = __ballot(found >= 0);
+      if (b) {
+        s = __builtin_amdgcn_readlane(found, __builtin_ctzll(b));
+      } else {
+        uint32_t bu = 0xFFFFFFFFu, bj = 0xFFFFFFFFu;
+        for (int j = lane; j < p.n_slots; j += 64)
+          if (used[j] < tick && used[j] < bu) {  // ascending j: the first keeps ties
+            bu = used[j];
+            bj = (uint32_t)j;
+          }
+        const uint32_t mu = wave_min_u32(bu);
+        s = (int)wave_min_u32(bu == mu ? bj : 0xFFFFFFFFu);
+        miss = 1;
+      }
+      if (lane == 0) {
+        own[s] = ek;
+        used[s] = tick;
+      }
+      __syncthreads();
+    }
+    if (lane == k) {
+      my_slot = s;
+      my_miss = miss;
+    }
+  }
+  if (lane < p.K) {
+    p.slot[lane] = my_slot;
+    const uint8_t *slot_rec = p.cache + (size_t)(my_slot >= 0 ? my_slot : 0) * p.stride;
+    const uint8_t *host_rec = p.host_dev + (size_t)(e >= 0 ? e : 0) * p.stride;
+    p.rec_src[lane] = reinterpret_cast<uint64_t>(my_miss ? host_rec : slot_rec);
+    p.rec_fill[lane] = my_miss ? reinterpret_cast<uint64_t>(slot_rec) : 0ull;
+  }
+  for (int j = lane; j < p.n_slots; j += 64) {
+    if (used[j] == tick) {
+      g_own[j] = own[j];
+      g_used[j] = tick;
+    }
+  }
+  const int n_miss = __builtin_popcountll(__ballot(lane < p.K && my_miss));
+  const int n_valid = __builtin_popcountll(__ballot(lane < p.K && my_slot >= 0));
+  if (lane == 0) {
+    st->tick = tick;
+    st->hits += (unsigned long long)(n_valid - n_miss);
+    st->misses += (unsigned long long)n_miss;
+    st->bytes += (unsigned long long)n_miss * p.record_bytes;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_tier_reset(uint8_t *state, int n_slots) {
+  TierState *st = reinterpret_cast<TierState *>(state);
+  int32_t *own = reinterpret_cast<int32_t *>(state + kTierOwnerOff);
+  uint32_t *used = reinterpret_cast<uint32_t *>(own + n_slots);
+  for (int j = threadIdx.x; j < n_slots; j += kBlock) {
+    own[j] = -1;
+    used[j] = 0u;
+  }
+  if (threadIdx.x == 0) {
+    st->tick = 0u;
+    st->pad[0] = 0u;
+    st->hits = st->misses = st->bytes = 0ull;
   }
 }
 
@@ -945,7 +1103,13 @@ hipError_t launch_gateup(const GateUpParams &p0, hipStream_t s) {
   p.waves_per_expert = (p.I + p.rows_per_wave - 1) / p.rows_per_wave;
   p.n_shared_blocks = p.with_shared ? (p.waves_per_expert + 3) / 4 : 0;
   const int waves = p.waves_per_expert * p.n;
-  const dim3 grid(p.n_shared_blocks + (waves + 3) / 4);
+  p.n_copy_blocks = 0;
+  if (p.rec_fill) {  // the tier's down-section copies: about 36 KiB per workgroup
+    const size_t bytes = (size_t)p.H * p.I * p.bits / 8 + (size_t)p.H * (p.I / kGroup) * 4;
+    p.copy_blocks_per_entry = (int)((bytes + 36863) / 36864);
+    p.n_copy_blocks = p.copy_blocks_per_entry * p.n;
+  }
+  const dim3 grid(p.n_shared_blocks + (waves + 3) / 4 + p.n_copy_blocks);
 #define MOE_GU(BITS, XS)                                                                        \
   do {                                                                                           \
     if constexpr (gateup_x_in_lds(BITS, XS)) {                                                   \
@@ -1020,6 +1184,16 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
     if (bits == 4) { MOE_DY(4); } else { MOE_DY(2); }
 #undef MOE_DY
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_tier_route(const TierRouteParams &p, hipStream_t s) {
+  MOE_LAUNCH(k_tier_route, dim3(1), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_tier_reset(uint8_t *state, int n_slots, hipStream_t s) {
+  MOE_LAUNCH(k_tier_reset, dim3(1), dim3(kBlock), 0, s, state, n_slots);
   return hipGetLastError();
 }
 

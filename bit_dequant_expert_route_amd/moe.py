@@ -79,12 +79,13 @@ def _load():
                                  C.c_double, C.c_double, P]),
         "moe_zero": (I, [P, Z, P]),
         "moe_gdn_step": (I, [I, I, I, I, P, P, P, P, P, P, P, P]),
-        "moe_tier_create": (I, [P, I, Z, P, I, C.POINTER(P)]),
+        "moe_tier_state_bytes": (Z, [I, I]),
+        "moe_tier_create": (I, [P, I, Z, P, I, P, C.POINTER(P)]),
         "moe_tier_destroy": (I, [P]),
-        "moe_tier_assign": (I, [P, P, I, P, P]),
+        "moe_tier_reset": (I, [P, P]),
         "moe_tier_layer_decode": (I, [C.POINTER(LayerStruct), P, I, P, P, P, P, P, P, Z, P]),
-        "moe_tier_stats": (I, [P, C.POINTER(C.c_ulonglong), C.POINTER(C.c_ulonglong),
-                               C.POINTER(C.c_ulonglong)]),
+        "moe_tier_stats": (I, [P, P, C.POINTER(C.c_ulonglong), C.POINTER(C.c_ulonglong),
+                               C.POINTER(C.c_ulonglong), P]),
         "moe_profile_begin": (I, [I]),
         "moe_profile_end": (I, [C.POINTER(C.c_float), C.POINTER(C.c_int), I, C.POINTER(C.c_int)]),
     }
@@ -342,30 +343,43 @@ def zero(t, stream=None):
 
 class Tier:
     """Host-memory expert tier (moe_tier_*): `host` holds the layer's E routed
-    records (a page-locked CPU uint8 tensor, or any host address), `cache` is
-    a CUDA uint8 tensor of n_slots * stride bytes.  Both must outlive the
-    tier."""
+    records (a page-locked CPU uint8 tensor), `cache` is a CUDA uint8 tensor of
+    n_slots * stride bytes, and the tier's device state is allocated here (a
+    CUDA tensor) and reset.  host and cache must outlive the tier."""
 
-    def __init__(self, host, n_experts: int, stride: int, cache, n_slots: int, host_ptr: int | None = None):
-        self.host, self.cache = host, cache
+    def __init__(self, host, n_experts: int, stride: int, cache, n_slots: int,
+                 host_ptr: int | None = None, cache_ptr: int | None = None,
+                 state_ptr: int | None = None, reset: bool = True):
+        self.host, self.cache, self.n_slots = host, cache, n_slots
+        nb = int(_lib.moe_tier_state_bytes(n_experts, n_slots))
+        self.state = None
+        if state_ptr is None:
+            self.state = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+            state_ptr = self.state.data_ptr()
         hp = host_ptr if host_ptr is not None else host.data_ptr()
-        cp = cache if isinstance(cache, int) else _ptr(cache)
+        cp = cache_ptr if cache_ptr is not None else _ptr(cache)
         h = C.c_void_p()
-        _check(_lib.moe_tier_create(hp, n_experts, stride, cp, n_slots, C.byref(h)), "moe_tier_create")
+        _check(_lib.moe_tier_create(hp, n_experts, stride, cp, n_slots, state_ptr, C.byref(h)),
+               "moe_tier_create")
         self.h = h
+        if reset:
+            self.reset()
 
-    def assign(self, ids):
-        n = len(ids)
-        a = (C.c_int32 * max(n, 1))(*ids)
-        sl = (C.c_int32 * max(n, 1))()
-        ms = (C.c_int32 * max(n, 1))()
-        _check(_lib.moe_tier_assign(self.h, a, n, sl, ms), "moe_tier_assign")
-        return list(sl)[:n], list(ms)[:n]
+    def reset(self, stream=None):
+        _check(_lib.moe_tier_reset(self.h, _stream(stream)), "moe_tier_reset")
 
-    def stats(self):
+    def stats(self, stream=None):
+        """(hits, misses, record bytes read from host memory) since the reset."""
         h, m, b = C.c_ulonglong(), C.c_ulonglong(), C.c_ulonglong()
-        _check(_lib.moe_tier_stats(self.h, C.byref(h), C.byref(m), C.byref(b)), "moe_tier_stats")
+        _check(_lib.moe_tier_stats(self.h, _stream(stream), C.byref(h), C.byref(m), C.byref(b), None),
+               "moe_tier_stats")
         return int(h.value), int(m.value), int(b.value)
+
+    def slots(self, stream=None):
+        """The expert in each slot (-1: empty)."""
+        own = (C.c_int32 * self.n_slots)()
+        _check(_lib.moe_tier_stats(self.h, _stream(stream), None, None, None, own), "moe_tier_stats")
+        return list(own)
 
     def layer_decode(self, layer: "Layer", x, h_res, h_out, topk_idx, topk_w, ws=None, stream=None):
         ws, wp, wb = _ws(layer, ws, 1)

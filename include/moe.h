@@ -228,49 +228,55 @@ int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *up
                      void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------- */
-/* host-memory expert tier ([openclawradar] "SSD expert streaming" and      */
-/* [a2a-fr] "Technical deep dive": only the routed experts of a token are   */
-/* read, on demand, after the routing; the OS page cache serves repeats)    */
+/* host-memory expert tier ([openclawradar] "SSD expert streaming",         */
+/* "Pipeline performance" and "Architecture constraint"; [a2a-fr] "Technical */
+/* deep dive / 1": only the routed experts of a token are read, on demand,   */
+/* after the routing, and a cache (the OS page cache on the pages) serves    */
+/* repeats)                                                                  */
 /* ---------------------------------------------------------------------- */
 typedef struct moe_tier_s *moe_tier_t;
+/* Device bytes of a tier's state: a tick, the hit / miss / byte counters and
+ * the owner and last use of every slot (0 for invalid sizes). */
+size_t moe_tier_state_bytes(int n_experts, int n_slots);
 /* A cache of n_slots routed-expert records in device memory in front of all
- * E records of one layer in host memory.
- *   host_records  E records, expert_stride bytes apart, caller-owned host
- *                 memory (page-locked, e.g. hipHostMalloc, for the copies to
- *                 be asynchronous)
- *   cache         n_slots x expert_stride bytes of device memory,
- *                 caller-owned, 256-byte aligned
- * K <= 8 <= n_slots <= E <= 1024; expert_stride a multiple of 256.  Slots are
- * replaced least recently used first.  The tier object is host bookkeeping
- * (no device or page-locked memory is allocated; the routing is read back
- * into the object itself); one stream at a time may use a tier. */
+ * E records of one layer in host memory, managed on the device.
+ *   host_records  E records, expert_stride bytes apart, caller-owned
+ *                 page-locked host memory the device can read (hipHostMalloc;
+ *                 a pinned torch tensor); MOE_EINVAL for pageable memory
+ *   cache         n_slots x expert_stride bytes of device memory
+ *   state         moe_tier_state_bytes(E, n_slots) bytes of device memory;
+ *                 moe_tier_reset initialises it before the first decode
+ * All caller-owned, 256-byte aligned, outliving the tier.  K <= 8 <= n_slots
+ * <= E <= 1024.  The handle holds the pointers and shapes (host memory, no
+ * device memory is allocated).  One stream at a time may use a tier. */
 int moe_tier_create(const void *host_records, int n_experts, size_t expert_stride,
-                    void *cache, int n_slots, moe_tier_t *out);
+                    void *cache, int n_slots, void *state, moe_tier_t *out);
 int moe_tier_destroy(moe_tier_t t);
-/* The slots of n expert ids (host arrays, 0 <= n <= n_slots): slots[i] holds
- * expert ids[i] after the call, miss[i] (may be NULL) is 1 when it had to be
- * brought in.  Bookkeeping only, no copy is issued; moe_tier_layer_decode
- * calls it with the routing of each token. */
-int moe_tier_assign(moe_tier_t t, const int32_t *ids, int n, int32_t *slots, int32_t *miss);
+/* Empty the cache and zero the counters (a kernel on `stream`). */
+int moe_tier_reset(moe_tier_t t, void *stream);
 /* moe_layer_decode for one token with the routed experts read through the
- * tier: router + top-K on the device, the K ids to the host (the call waits
- * for them once, so it cannot be captured into a graph: MOE_EINVAL), the
- * missing records copied into their slots (host to device, on `stream`), then
- * gate/up and down + combine on the cached records.  L->experts and
- * L->expert_stride are not used; the layer's router, gate vector and shared
- * expert are.  The outputs (topk_idx holds expert ids, not slots) equal those
- * of moe_layer_decode.
- * Exceptions to the conventions above, both forced by the host read-back:
- * the call synchronises `stream` once per token, and a failure found after
- * the read-back (a routing id outside [0, E), which only NaN logits can
- * produce) returns MOE_EINVAL with the router and top-K kernels already
- * enqueued and no expert kernel after them. */
+ * tier, entirely on the device (no host wait; the call can be captured into
+ * a graph): the router, then one kernel that takes the top K and gives each
+ * selected expert its slot -- the slot holding it (a hit), else the least
+ * recently used slot this token has not taken (never-used slots first, the
+ * lowest slot among equal uses) -- then the gate/up launch, which reads a
+ * hit's gate/up rows from its slot and a miss's straight from host memory,
+ * writing them into the slot as it reads them, while extra workgroups of the
+ * same launch copy each miss's down rows from host memory into its slot;
+ * then down + combine on the slots.  A miss therefore crosses the host link
+ * once, and its transfer overlaps the hits' and the shared expert's work.
+ * L->experts and L->expert_stride are not used.  The outputs (topk_idx holds
+ * expert ids) equal those of moe_layer_decode. */
 int moe_tier_layer_decode(const moe_layer_t *L, moe_tier_t t, moe_dtype x_dtype, const void *x,
                           const float *h_res, float *h_out, int32_t *topk_idx, float *topk_w,
                           void *ws, size_t ws_bytes, void *stream);
-/* Hits, misses and record bytes copied so far (any pointer may be NULL). */
-int moe_tier_stats(moe_tier_t t, unsigned long long *hits, unsigned long long *misses,
-                   unsigned long long *bytes_copied);
+/* Hits, misses and record bytes read from host memory since the last reset,
+ * and (if slot_owner is not NULL) the expert in each slot ([n_slots], -1 for
+ * an empty slot); any output may be NULL.  A query outside the decode path:
+ * it copies the state to the host and waits for `stream`. */
+int moe_tier_stats(moe_tier_t t, void *stream, unsigned long long *hits,
+                   unsigned long long *misses, unsigned long long *bytes_read,
+                   int32_t *slot_owner);
 
 /* ---------------------------------------------------------------------- */
 /* HIP graphs ([openclawradar] "Deferred GPU expert compute": the expert     */

@@ -1,19 +1,21 @@
-"""Host bookkeeping of the expert tier (moe_tier_create / _assign / _stats),
-checked against a plain least-recently-used model; no device is touched (the
-tier only records addresses until a decode call)."""
-import random
+"""Host-side checks of the expert tier: argument validation of moe_tier_create
+and the state size (no device is touched: every call here fails its checks
+or only computes a size), and the least-recently-used model the GPU tests
+compare the device's slot table against."""
+import ctypes as C
 
 import pytest
 
 moe = pytest.importorskip("bit_dequant_expert_route_amd.moe")
 
-HOST, CACHE, STRIDE = 0x10000, 0x100000, 256
+HOST, CACHE, STATE, STRIDE = 0x10000, 0x100000, 0x200000, 256
 
 
 class LRUModel:
-    """Slots hold experts; a call takes one tick; a miss takes the slot with
-    the oldest last use among those this call has not used (never-used slots
-    first, lowest index on ties)."""
+    """Slots hold experts; a token takes one tick; its experts are taken in
+    the order of the selection; a miss takes the slot with the oldest last use
+    among those this token has not used (never-used slots first, lowest index
+    on ties)."""
 
     def __init__(self, n_slots):
         self.owner = [-1] * n_slots
@@ -37,53 +39,41 @@ class LRUModel:
         return slots, miss
 
 
-@pytest.mark.parametrize("n_experts,n_slots,k,seed", [(32, 8, 4, 1), (512, 64, 4, 2), (16, 8, 8, 3)])
-def test_assign_matches_lru_model(n_experts, n_slots, k, seed):
-    rng = random.Random(seed)
-    t = moe.Tier(None, n_experts, STRIDE, CACHE, n_slots, host_ptr=HOST)
-    model = LRUModel(n_slots)
-    hot = list(range(0, n_experts, max(1, n_experts // (2 * n_slots))))
-    total = model_misses = 0
-    for step in range(300):
-        pool = hot if rng.random() < 0.7 else list(range(n_experts))
-        ids = rng.sample(pool, k) if len(pool) >= k else rng.sample(range(n_experts), k)
-        slots, miss = t.assign(ids)
-        want_slots, want_miss = model.assign(ids)
-        assert (slots, miss) == (want_slots, want_miss), (step, ids, slots, want_slots)
-        assert len(set(slots)) == len(ids)  # distinct slots within a call
-        total += len(ids)
-        model_misses += sum(want_miss)
-    hits, misses, copied = t.stats()
-    assert (hits, misses) == (total - model_misses, model_misses)
-    assert 0 < misses < total
-    assert copied == 0  # assign alone copies nothing
-    t.close()
-
-
-def test_repeat_is_hit_and_eviction_order():
-    t = moe.Tier(None, 16, STRIDE, CACHE, 8, host_ptr=HOST)
-    s1, m1 = t.assign([0, 1, 2, 3, 4, 5, 6, 7])
+def test_lru_model_eviction_order():
+    m = LRUModel(8)
+    s1, m1 = m.assign([0, 1, 2, 3, 4, 5, 6, 7])
     assert m1 == [1] * 8 and s1 == list(range(8))
-    s2, m2 = t.assign([3, 9])  # 3 hits; 9 evicts the oldest slot not used now
-    assert m2 == [0, 1] and s2[0] == s1[3] and s2[1] == 0
-    s3, m3 = t.assign([0])  # 0 was evicted by 9
-    assert m3 == [1] and s3[0] == 1
-    assert t.stats()[:2] == (1, 10)
-    t.close()
+    s2, m2 = m.assign([3, 9])  # 3 hits; 9 evicts the oldest slot not used now
+    assert m2 == [0, 1] and s2 == [3, 0]
+    s3, m3 = m.assign([0, 9])  # 0 was evicted by 9 and takes the next oldest
+    assert m3 == [1, 0] and s3 == [1, 0]
+
+
+def test_state_bytes():
+    assert moe.lib.moe_tier_state_bytes(512, 128) == 64 + 128 * 8 + 192  # rounded to 256
+    assert moe.lib.moe_tier_state_bytes(512, 4) == 0     # fewer slots than the largest K
+    assert moe.lib.moe_tier_state_bytes(16, 17) == 0     # more slots than experts
+    assert moe.lib.moe_tier_state_bytes(2000, 64) == 0   # more experts than supported
+
+
+def _create(host=HOST, e=16, stride=STRIDE, cache=CACHE, slots=8, state=STATE):
+    h = C.c_void_p()
+    return moe.lib.moe_tier_create(host, e, stride, cache, slots, state, C.byref(h))
 
 
 def test_tier_validation():
-    with pytest.raises(moe.MoeError):
-        moe.Tier(None, 16, STRIDE, CACHE, 4, host_ptr=HOST)  # fewer slots than the largest K
-    with pytest.raises(moe.MoeError):
-        moe.Tier(None, 16, STRIDE, CACHE, 17, host_ptr=HOST)  # more slots than experts
-    with pytest.raises(moe.MoeError):
-        moe.Tier(None, 16, STRIDE + 16, CACHE, 8, host_ptr=HOST)  # stride not 256-aligned
-    with pytest.raises(moe.MoeError):
-        moe.Tier(None, 16, STRIDE, CACHE + 8, 8, host_ptr=HOST)  # cache not 256-aligned
-    t = moe.Tier(None, 16, STRIDE, CACHE, 8, host_ptr=HOST)
-    with pytest.raises(moe.MoeError):
-        t.assign([16])
-    with pytest.raises(moe.MoeError):
-        t.assign(list(range(9)))  # more ids than slots
-    t.close()
+    assert _create(slots=4) == moe.MOE_EINVAL       # fewer slots than the largest K
+    assert _create(slots=17) == moe.MOE_EINVAL      # more slots than experts
+    assert _create(e=0) == moe.MOE_EINVAL
+    assert _create(host=0) == moe.MOE_EINVAL
+    assert _create(state=0) == moe.MOE_EINVAL
+    assert _create(stride=STRIDE + 16) == moe.MOE_EALIGN
+    assert _create(cache=CACHE + 8) == moe.MOE_EALIGN
+    assert _create(state=STATE + 64) == moe.MOE_EALIGN
+    # an address the device cannot map (not page-locked host memory)
+    buf = C.create_string_buffer(4096 + 256)
+    aligned = (C.addressof(buf) + 255) // 256 * 256
+    assert _create(host=aligned) == moe.MOE_EINVAL
+    assert "page-locked" in moe.lib.moe_last_error().decode()
+    assert moe.lib.moe_tier_destroy(None) == moe.MOE_EINVAL
+    assert moe.lib.moe_tier_reset(None, None) == moe.MOE_EINVAL
