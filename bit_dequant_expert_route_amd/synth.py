@@ -51,6 +51,14 @@ SEC_GATE_SB, SEC_UP_SB, SEC_DOWN_SB = 3, 4, 5
 STREAM_ROUTER, STREAM_GATEVEC, STREAM_X, STREAM_HRES, STREAM_UPDATE, STREAM_H0 = 1, 2, 3, 4, 5, 6
 STREAM_TOKEN_BASE, STREAM_TOKEN = 7, 8
 STREAM_GDN = 9
+STREAM_GDN_STATE = 10
+
+# generator ids of a layer's linear-attention projections: two records of the
+# expert format with hidden = H and inter = D = heads * head width
+#   qko: gate = W_q [D][H], up = W_k [D][H], down = W_o [H][D]
+#   vab: gate = W_v [D][H], up rows 0..2 heads-1 = W_alpha, W_beta
+GDN_QKO_GEN_ID = (1 << 20) + 1
+GDN_VAB_GEN_ID = (1 << 20) + 2
 
 GROUP = 64
 
@@ -276,6 +284,9 @@ class LayerConfig:
     x_dtype: str           # "f32" | "bf16"
     n_layers: int = 1
     n_tokens: int = 1
+    gdn_heads: int = 0     # linear-attention heads of a stack (0: none)
+    gdn_head_dim: int = 0
+    gdn_bits: int = 4
 
     @property
     def record_bytes(self) -> int:
@@ -304,9 +315,16 @@ CONFIGS = {
     "q4_stack": LayerConfig("q4_stack", 4096, 1024, 512, 4, 4, 4, "bf16", "bf16", "f32", n_layers=60),
     # 16-token micro-batch on the Qwen-shaped layer
     "q4_batch16": LayerConfig("q4_batch16", 4096, 1024, 512, 4, 4, 4, "bf16", "bf16", "bf16", n_tokens=16),
+    # the same stack with the linear-attention block of the pages in 45 of its
+    # layers (64 heads, a 128 x 128 state each, 4-bit projections); the other
+    # 15 keep the random update standing in for full attention
+    "q4_stack_gdn": LayerConfig("q4_stack_gdn", 4096, 1024, 512, 4, 4, 4, "bf16", "bf16", "f32",
+                                n_layers=60, gdn_heads=64, gdn_head_dim=128),
     # small parity cases of the stack and batch paths
     "tiny_stack": LayerConfig("tiny_stack", 256, 128, 16, 2, 4, 4, "bf16", "bf16", "f32", n_layers=8),
     "tiny_batch": LayerConfig("tiny_batch", 256, 128, 16, 2, 4, 4, "bf16", "bf16", "bf16", n_tokens=7),
+    "tiny_stack_gdn": LayerConfig("tiny_stack_gdn", 256, 128, 16, 2, 4, 4, "bf16", "bf16", "f32",
+                                  n_layers=8, gdn_heads=4, gdn_head_dim=32),
 }
 
 ROUTER_STD = 0.02
@@ -383,3 +401,24 @@ def gdn_inputs(seed: int, n_seq: int, n_heads: int, d_k: int, d_v: int, step: in
     state = normals(shape + (d_v, d_k), 0.1, seed, STREAM_GDN, 4)
     f = lambda a: np.ascontiguousarray(a, dtype=np.float32)  # noqa: E731
     return f(q), f(k), f(v), f(alpha), f(beta), f(state)
+
+
+# ----------------------------------------------------------------------------
+# linear-attention layers of a stack
+# ----------------------------------------------------------------------------
+def is_attention_layer(layer: int) -> bool:
+    """Every fourth layer is a full-attention layer (15 of 60) and the others
+    are linear-attention layers (45 of 60), the mix the pages give."""
+    return layer % 4 == 3
+
+
+def gdn_records(seed: int, layer: int, hidden: int, n_heads: int, d_head: int, bits: int):
+    """The (qko, vab) projection records of one linear-attention layer."""
+    D = n_heads * d_head
+    return (make_record(seed, layer, GDN_QKO_GEN_ID, hidden, D, bits),
+            make_record(seed, layer, GDN_VAB_GEN_ID, hidden, D, bits))
+
+
+def gdn_state0(seed: int, layer: int, n_heads: int, d_head: int, attempt: int = 0) -> np.ndarray:
+    """fp32 N(0, 0.1^2) state [heads][d][d] carried in from earlier tokens."""
+    return normals((n_heads, d_head, d_head), 0.1, seed, STREAM_GDN_STATE, layer, attempt).astype(np.float32)

@@ -71,6 +71,9 @@ class Oracle:
         L.oracle_gdn_step.restype = None
         L.oracle_gdn_step.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, _dp, _dp, _dp, _dp,
                                       _dp, _dp, _dp]
+        L.oracle_gdn_block.restype = None
+        L.oracle_gdn_block.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, _u8p, _u8p, _dp, _dp,
+                                       _dp, _dp, _dp]
         L.oracle_layer.restype = None
         L.oracle_layer.argtypes = [
             C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
@@ -181,6 +184,25 @@ class Oracle:
         o = np.empty((n_seq, n_heads, d_v))
         self._L.oracle_gdn_step(n_seq, n_heads, d_k, d_v, q, k, v, a, b, S, o)
         return S, o
+
+    def gdn_block(self, rec_qko, rec_vab, hidden, n_heads, d_head, bits, h, state):
+        """One linear-attention block for one token: x = RMSNorm(h), the
+        quantised q/k/v/alpha/beta projections, unit-length q and k per head,
+        sigmoid gates, the gated delta-rule step, and h + W_o o.  Returns dict
+        (proj [3D + 2 n_heads], o [D], h_out [H], state [n_heads][d][d]); the
+        inputs are not modified."""
+        D = n_heads * d_head
+        rq = np.ascontiguousarray(rec_qko, dtype=np.uint8).reshape(-1)
+        rv = np.ascontiguousarray(rec_vab, dtype=np.uint8).reshape(-1)
+        need = self.record_bytes(hidden, D, bits)
+        assert rq.size >= need and rv.size >= need
+        h = np.ascontiguousarray(h, dtype=np.float64)
+        S = np.array(state, dtype=np.float64, copy=True, order="C").reshape(n_heads, d_head, d_head)
+        proj = np.empty(3 * D + 2 * n_heads)
+        o = np.empty(D)
+        h_out = np.empty(hidden)
+        self._L.oracle_gdn_block(hidden, n_heads, d_head, bits, rq, rv, h, S, proj, o, h_out)
+        return dict(proj=proj, o=o, h_out=h_out, state=S)
 
     # -- composite -------------------------------------------------------
     def route(self, router, router_dtype, gate_vec, gate_dtype, x, top_k, renorm):

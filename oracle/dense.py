@@ -88,3 +88,29 @@ def layer(*, hidden, inter, n_experts, top_k, bits_routed, bits_shared, renorm,
     Y = np.stack(ys)
     out = np.asarray(h_res, dtype=np.float64) + w @ Y[:top_k] + sigma * Y[top_k]
     return dict(logits=logits, p=p, idx=idx, w=w, sigma=sigma, h=np.stack(hs), y=Y, out=out)
+
+
+def gdn_block(rec_qko, rec_vab, hidden, n_heads, d_head, bits, h, state):
+    """The linear-attention block on dense matrices: x = RMSNorm(h), the
+    projections as matrix products, unit-length q and k per head, sigmoid
+    gates, the delta rule in its closed matrix form
+    S_new = alpha S (I - beta k k^T) + beta v k^T, o = S_new q, and h + W_o o."""
+    D = n_heads * d_head
+    Wq, Wk, Wo = expert_matrices(rec_qko, hidden, D, bits)
+    Wv, Wab, _ = expert_matrices(rec_vab, hidden, D, bits)
+    h = np.asarray(h, dtype=np.float64)
+    x = h / np.sqrt(np.mean(h * h) + 1e-6)
+    q = (Wq @ x).reshape(n_heads, d_head)
+    k = (Wk @ x).reshape(n_heads, d_head)
+    v = (Wv @ x).reshape(n_heads, d_head)
+    ab = Wab[:2 * n_heads] @ x
+    q = q / np.sqrt(np.sum(q * q, axis=1, keepdims=True) + 1e-6)
+    k = k / np.sqrt(np.sum(k * k, axis=1, keepdims=True) + 1e-6)
+    alpha = 1.0 / (1.0 + np.exp(-ab[:n_heads]))
+    beta = 1.0 / (1.0 + np.exp(-ab[n_heads:]))
+    S = np.asarray(state, dtype=np.float64).reshape(n_heads, d_head, d_head)
+    eye = np.eye(d_head)
+    Sn = np.stack([alpha[i] * S[i] @ (eye - beta[i] * np.outer(k[i], k[i]))
+                   + beta[i] * np.outer(v[i], k[i]) for i in range(n_heads)])
+    o = np.einsum("hij,hj->hi", Sn, q).reshape(D)
+    return dict(o=o, h_out=h + Wo @ o, state=Sn, proj=np.concatenate([(Wq @ x), (Wk @ x), (Wv @ x), ab]))

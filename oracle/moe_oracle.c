@@ -36,7 +36,13 @@
  *   - the linear-attention decode step is the gated delta rule in the order
  *     of the pages' BLAS calls: scale the state, u = S k, S += beta (v - u) k^T,
  *     o = S q, with q, k, v, alpha, beta given (their projections are not part
- *     of this step).
+ *     of this step);
+ *   - a linear-attention block around it (the pages give only the head count
+ *     and state size): x = RMSNorm(h); q, k, v and one alpha and one beta
+ *     logit per head are rows of quantised projections of x; q and k are
+ *     scaled to unit length per head (eps 1e-6 under the root), alpha and
+ *     beta are sigmoids of their logits; the block adds the quantised output
+ *     projection of o to the residual stream.
  */
 #include <math.h>
 #include <stdint.h>
@@ -368,4 +374,69 @@ void oracle_gdn_step(int n_seq, int n_heads, int d_k, int d_v, const double *q,
             }
         }
     }
+}
+
+/* ------------------------------------------------------------------ */
+/* linear-attention block around the decode step                       */
+/* ------------------------------------------------------------------ */
+/* One gated-delta-rule block for one token ([openclawradar] "Pipeline
+ * performance": CMD1 runs the attention projections and the delta net;
+ * "Accelerate BLAS for linear attention": 64 heads, a 128x128 state each).
+ * D = n_heads * d_head.  The projections are quantised [rows][cols]
+ * matrices in two records of the expert format (hidden = H, inter = D):
+ *   rec_qko: gate = W_q [D][H], up = W_k [D][H], down = W_o [H][D]
+ *   rec_vab: gate = W_v [D][H], up rows 0..n_heads-1 = W_alpha,
+ *            rows n_heads..2 n_heads-1 = W_beta
+ * Steps, in order:
+ *   x = RMSNorm(h);  q = W_q x;  k = W_k x;  v = W_v x;
+ *   a = W_alpha x;  b = W_beta x;
+ *   per head: q_h /= sqrt(|q_h|^2 + 1e-6);  k_h /= sqrt(|k_h|^2 + 1e-6);
+ *             alpha_h = 1 / (1 + exp(-a_h));  beta_h = 1 / (1 + exp(-b_h));
+ *   the decode step of every head on `state` ([n_heads][d_head][d_head],
+ *   updated in place) -> o [D];
+ *   h_out = h + W_o o.
+ * Also returns the projections (proj: q, k, v as projected, then a, b) and
+ * o, for per-stage checks.  proj holds 3 D + 2 n_heads values. */
+void oracle_gdn_block(int hidden, int n_heads, int d_head, int bits,
+                      const uint8_t *rec_qko, const uint8_t *rec_vab,
+                      const double *h, double *state, double *proj,
+                      double *o, double *h_out)
+{
+    const int D = n_heads * d_head;
+    const oracle_layout lay = layout_of(hidden, D, bits);
+    double *x = (double *)malloc(sizeof(double) * (size_t)hidden);
+    double *q = (double *)malloc(sizeof(double) * (size_t)D);
+    double *k = (double *)malloc(sizeof(double) * (size_t)D);
+    double *alpha = (double *)malloc(sizeof(double) * (size_t)n_heads);
+    double *beta = (double *)malloc(sizeof(double) * (size_t)n_heads);
+    double *y = (double *)malloc(sizeof(double) * (size_t)hidden);
+    oracle_rmsnorm(h, hidden, 1e-6, x);
+    oracle_qmatvec((const uint32_t *)(rec_qko + lay.gate_codes),
+                   (const uint32_t *)(rec_qko + lay.gate_sb), D, hidden, bits, x, proj);
+    oracle_qmatvec((const uint32_t *)(rec_qko + lay.up_codes),
+                   (const uint32_t *)(rec_qko + lay.up_sb), D, hidden, bits, x, proj + D);
+    oracle_qmatvec((const uint32_t *)(rec_vab + lay.gate_codes),
+                   (const uint32_t *)(rec_vab + lay.gate_sb), D, hidden, bits, x, proj + 2 * D);
+    oracle_qmatvec((const uint32_t *)(rec_vab + lay.up_codes),
+                   (const uint32_t *)(rec_vab + lay.up_sb), 2 * n_heads, hidden, bits, x,
+                   proj + 3 * D);
+    for (int hd = 0; hd < n_heads; ++hd) {
+        const double *qh = proj + (size_t)hd * d_head;
+        const double *kh = proj + D + (size_t)hd * d_head;
+        double nq = 0.0, nk = 0.0;
+        for (int j = 0; j < d_head; ++j) nq += qh[j] * qh[j];
+        for (int j = 0; j < d_head; ++j) nk += kh[j] * kh[j];
+        const double rq = 1.0 / sqrt(nq + 1e-6), rk = 1.0 / sqrt(nk + 1e-6);
+        for (int j = 0; j < d_head; ++j) {
+            q[(size_t)hd * d_head + j] = qh[j] * rq;
+            k[(size_t)hd * d_head + j] = kh[j] * rk;
+        }
+        alpha[hd] = 1.0 / (1.0 + exp(-proj[3 * D + hd]));
+        beta[hd] = 1.0 / (1.0 + exp(-proj[3 * D + n_heads + hd]));
+    }
+    oracle_gdn_step(1, n_heads, d_head, d_head, q, k, proj + 2 * D, alpha, beta, state, o);
+    oracle_qmatvec((const uint32_t *)(rec_qko + lay.down_codes),
+                   (const uint32_t *)(rec_qko + lay.down_sb), hidden, D, bits, o, y);
+    for (int i = 0; i < hidden; ++i) h_out[i] = h[i] + y[i];
+    free(x); free(q); free(k); free(alpha); free(beta); free(y);
 }

@@ -177,6 +177,65 @@ def make_stack_case(cfg: synth.LayerConfig, seed: int, n_layers: int | None = No
 
 
 # ----------------------------------------------------------------------------
+# stacks with linear-attention layers: in those layers the block's output
+# replaces the update, and the state carried in from earlier tokens is what
+# is redrawn until the layer's top-K gap is large enough
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class GdnStackCase:
+    cfg: synth.LayerConfig
+    seed: int
+    n_layers: int
+    h0: np.ndarray              # fp32 [H]
+    updates: np.ndarray         # bf16 bits [L][H] (zero rows in linear-attention layers)
+    states0: list               # per layer: fp32 [heads][d][d] initial state, or None
+    states: list                # per layer: fp64 state after the token, or None
+    attempts: list
+    routers: list
+    gates: list
+    idx: np.ndarray
+    w: np.ndarray
+    h: np.ndarray               # fp64 [H] after the last layer
+
+
+def make_gdn_stack_case(cfg: synth.LayerConfig, seed: int, n_layers: int | None = None,
+                        renorm: bool = True, orc: oracle.Oracle | None = None) -> GdnStackCase:
+    orc = orc or oracle.get()
+    L = n_layers or cfg.n_layers
+    H, nh, dh, gb = cfg.hidden, cfg.gdn_heads, cfg.gdn_head_dim, cfg.gdn_bits
+    h = synth.stack_h0(cfg, seed).astype(np.float64)
+    h0 = h.astype(np.float32)
+    ups, s0s, ss, atts, routers, gates, idxs, ws = [], [], [], [], [], [], [], []
+    for l in range(L):
+        router = synth.router_weights(cfg, seed, l)
+        gate = synth.shared_gate_vector(cfg, seed, l)
+        attn = synth.is_attention_layer(l)
+        rq = rv = None
+        if not attn:
+            rq, rv = synth.gdn_records(seed, l, H, nh, dh, gb)
+        for attempt in range(1000):
+            if attn:
+                u = synth.layer_update(cfg, seed, l, attempt)
+                hr = h + synth.bf16_to_f32(u).astype(np.float64)
+                s0 = s1 = None
+            else:
+                u = np.zeros(H, dtype=np.uint16)
+                s0 = synth.gdn_state0(seed, l, nh, dh, attempt)
+                blk = orc.gdn_block(rq, rv, H, nh, dh, gb, h, s0.astype(np.float64))
+                hr, s1 = blk["h_out"], blk["state"]
+            x64 = orc.rmsnorm(hr, 1e-6)
+            if logit_gap(orc.router(router, cfg.router_dtype, x64), cfg.top_k) >= GAP:
+                break
+        else:
+            raise RuntimeError(f"layer {l}: no draw with a large enough logit gap")
+        route, h = layer_from_records(orc, cfg, seed, l, router, gate, x64, hr, renorm)
+        ups.append(u); s0s.append(s0); ss.append(s1); atts.append(attempt)
+        routers.append(router); gates.append(gate); idxs.append(route["idx"]); ws.append(route["w"])
+    return GdnStackCase(cfg, seed, L, h0, np.stack(ups), s0s, ss, atts, routers, gates,
+                        np.stack(idxs), np.stack(ws), h)
+
+
+# ----------------------------------------------------------------------------
 # correlated token batches
 # ----------------------------------------------------------------------------
 @dataclasses.dataclass

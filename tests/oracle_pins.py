@@ -476,4 +476,84 @@ def pin_gdn_matrix_form(orc):
             assert np.allclose(o[s_, h], want @ q[s_, h], rtol=1e-12, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------
+# linear-attention block around the decode step
+# ----------------------------------------------------------------------------
+def _gdn_block_inputs(rng, H=128, n_heads=2, d_head=32, bits=4):
+    D = n_heads * d_head
+    rq, _ = random_record(rng, H, D, bits)
+    rv, _ = random_record(rng, H, D, bits)
+    h = rng.standard_normal(H)
+    S = 0.1 * rng.standard_normal((n_heads, d_head, d_head))
+    return rq, rv, h, S
+
+
+def pin_gdn_block_dense(orc):
+    """The whole block against its dense NumPy brute force (matrices
+    materialised, products by matmul, the delta rule in closed matrix form),
+    at 4 and 2 bits."""
+    for bits, seed in ((4, 21), (2, 22)):
+        rng = np.random.default_rng(seed)
+        H, nh, dh = 128, 2, 32
+        rq, rv, h, S = _gdn_block_inputs(rng, H, nh, dh, bits)
+        got = orc.gdn_block(rq, rv, H, nh, dh, bits, h, S)
+        want = dense.gdn_block(rq, rv, H, nh, dh, bits, h, S)
+        for key in ("proj", "o", "h_out", "state"):
+            assert rel_err(got[key], want[key]) < 1e-12, (bits, key, rel_err(got[key], want[key]))
+
+
+def pin_gdn_block_gates_and_unit_keys(orc):
+    """With zero gate rows (codes and biases 0) both gates are sigmoid(0) =
+    1/2 exactly; then, from the block's own projections, the new state must be
+    S/2 (I - k^ k^T/2) + v k^T/2 with k^ = k / sqrt(|k|^2 + 1e-6) per head, and
+    o = S_new q^: unit-length keys and queries, checked with numpy."""
+    rng = np.random.default_rng(23)
+    H, nh, dh, bits = 128, 2, 32, 4
+    D = nh * dh
+    rq, _ = random_record(rng, H, D, bits)
+    trip = []
+    for rows, cols in ((D, H), (D, H), (H, D)):
+        codes, s, b, _, _ = random_qmatrix(rng, rows, cols, bits)
+        trip.append((codes, s, b))
+    codes, s, b = trip[1]
+    codes[:2 * nh] = 0
+    b[:2 * nh] = 0
+    rv = build_record(trip[0], (codes, s, b), trip[2], H, D, bits)
+    h = rng.standard_normal(H)
+    S = 0.1 * rng.standard_normal((nh, dh, dh))
+    got = orc.gdn_block(rq, rv, H, nh, dh, bits, h, S)
+    proj = got["proj"]
+    assert np.array_equal(proj[3 * D:], np.zeros(2 * nh))
+    q = proj[:D].reshape(nh, dh)
+    k = proj[D:2 * D].reshape(nh, dh)
+    v = proj[2 * D:3 * D].reshape(nh, dh)
+    qh = q / np.sqrt(np.sum(q * q, axis=1, keepdims=True) + 1e-6)
+    kh = k / np.sqrt(np.sum(k * k, axis=1, keepdims=True) + 1e-6)
+    eye = np.eye(dh)
+    for i in range(nh):
+        want = 0.5 * S[i] @ (eye - 0.5 * np.outer(kh[i], kh[i])) + 0.5 * np.outer(v[i], kh[i])
+        assert np.allclose(got["state"][i], want, rtol=1e-12, atol=1e-13)
+        assert np.allclose(got["o"][i * dh:(i + 1) * dh], want @ qh[i], rtol=1e-12, atol=1e-13)
+
+
+def pin_gdn_block_zero_output_projection(orc):
+    """A zero output projection (codes and biases 0) leaves the residual
+    stream exactly as it was, whatever the state does."""
+    rng = np.random.default_rng(24)
+    H, nh, dh, bits = 128, 2, 32, 4
+    D = nh * dh
+    trip = []
+    for rows, cols in ((D, H), (D, H), (H, D)):
+        codes, s, b, _, _ = random_qmatrix(rng, rows, cols, bits)
+        trip.append((codes, s, b))
+    codes, s, b = trip[2]
+    rq = build_record(trip[0], trip[1], (np.zeros_like(codes), s, np.zeros_like(b)), H, D, bits)
+    rv, _ = random_record(rng, H, D, bits)
+    h = rng.standard_normal(H)
+    S = 0.1 * rng.standard_normal((nh, dh, dh))
+    got = orc.gdn_block(rq, rv, H, nh, dh, bits, h, S)
+    assert np.array_equal(got["h_out"], h)
+    assert not np.allclose(got["state"], S)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -44,6 +44,15 @@ MUTANTS = [
      "for (int j = 0; j < d_k; ++j) o += row[j] * kh[j];"),
     ("gdn_transposed_gemv", "for (int j = 0; j < d_k; ++j) u += row[j] * kh[j];",
      "for (int j = 0; j < d_k && j < d_v; ++j) u += S[(size_t)j * d_k + i] * kh[j];"),
+    ("gdn_block_no_qnorm", "q[(size_t)hd * d_head + j] = qh[j] * rq;", "q[(size_t)hd * d_head + j] = qh[j];"),
+    ("gdn_block_no_knorm", "k[(size_t)hd * d_head + j] = kh[j] * rk;", "k[(size_t)hd * d_head + j] = kh[j];"),
+    ("gdn_block_gates_swapped", "alpha[hd] = 1.0 / (1.0 + exp(-proj[3 * D + hd]));",
+     "alpha[hd] = 1.0 / (1.0 + exp(-proj[3 * D + n_heads + hd]));"),
+    ("gdn_block_no_residual", "h_out[i] = h[i] + y[i];", "h_out[i] = y[i];"),
+    ("gdn_block_unnormalised_x", "oracle_rmsnorm(h, hidden, 1e-6, x);",
+     "memcpy(x, h, sizeof(double) * (size_t)hidden);"),
+    ("gdn_block_v_from_k", "proj + 2 * D, alpha, beta, state, o);", "proj + D, alpha, beta, state, o);"),
+    ("gdn_block_out_reads_q", "hidden, D, bits, o, y);", "hidden, D, bits, q, y);"),
 ]
 
 
