@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--instances", type=int, default=128)
     ap.add_argument("--workload", default="q4_layer",
-                    choices=["q4_layer", "q2_layer", "q4_stack", "q4_batch16", "gdn_step", "q4_tier"])
+                    choices=["q4_layer", "q2_layer", "q4_stack", "q4_stack_gdn", "q4_batch16", "gdn_step",
+                             "q4_tier"])
     ap.add_argument("--tier-slots", type=int, default=128,
                     help="q4_tier: routed records the device cache holds")
     ap.add_argument("--tier-ar", type=float, default=0.95,
@@ -209,10 +210,24 @@ def cpu_model():
     return None
 
 
+def gdn_bytes_per_layer(cfg):
+    """HBM bytes of one linear-attention block for one token: the q/k/v
+    projections and the 2 heads gate rows, the output projection, the state
+    read and written."""
+    H, D, nh, b = cfg.hidden, cfg.gdn_heads * cfg.gdn_head_dim, cfg.gdn_heads, cfg.gdn_bits
+
+    def mat(rows, cols):
+        return rows * cols * b // 8 + rows * (cols // 64) * 4
+    state = nh * cfg.gdn_head_dim * cfg.gdn_head_dim * 4
+    return 3 * mat(D, H) + mat(2 * nh, H) + mat(H, D) + 2 * state + (3 * D + 2 * nh) * 4 * 2 + D * 4 * 2
+
+
 def bench_stack(cfg, args):
     """One token through the resident 60-layer stack (217 GB at 4 bits): a HIP
     graph of the whole stack, replayed; every layer has its own 512 experts, so
-    nothing is cache-resident.  Returns (ms per token, per-kernel live us)."""
+    nothing is cache-resident.  With cfg.gdn_heads, the linear-attention
+    layers (45 of 60) open with their block (own projections and 4 MiB
+    state).  Returns (ms per token, per-kernel live us)."""
     import torch
     from bit_dequant_expert_route_amd import moe, synth
     H, I, E, L = cfg.hidden, cfg.inter, cfg.n_experts, cfg.n_layers
@@ -220,8 +235,24 @@ def bench_stack(cfg, args):
     sb = synth.record_layout(H, I, cfg.bits_shared).total
     g = torch.Generator(device="cuda")
     g.manual_seed(3000)
-    layers, keep = [], []
+    layers, keep, gdn = [], [], []
+    use_gdn = cfg.gdn_heads > 0
+    D = cfg.gdn_heads * cfg.gdn_head_dim
     for l in range(L):
+        if use_gdn and not synth.is_attention_layer(l):
+            gb = synth.record_layout(H, D, cfg.gdn_bits).total
+            recs = []
+            for gid in (synth.GDN_QKO_GEN_ID, synth.GDN_VAB_GEN_ID):
+                r = torch.empty(gb, dtype=torch.uint8, device="cuda")
+                moe.fill_experts(r, gb, 1, 3000, l, gid, H, D, cfg.gdn_bits,
+                                 synth.dist_for_bits(cfg.gdn_bits))
+                recs.append(r)
+            st = torch.randn(cfg.gdn_heads, cfg.gdn_head_dim, cfg.gdn_head_dim, generator=g,
+                             device="cuda") * 0.1
+            gdn.append(dict(n_heads=cfg.gdn_heads, d_head=cfg.gdn_head_dim, bits=cfg.gdn_bits,
+                            rec_qko=recs[0], rec_vab=recs[1], state=st))
+        else:
+            gdn.append(None)
         pool = torch.empty(E * rb, dtype=torch.uint8, device="cuda")
         moe.fill_experts(pool, rb, E, 3000, l, 0, H, I, cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
         shared = torch.empty(sb, dtype=torch.uint8, device="cuda")
@@ -233,18 +264,24 @@ def bench_stack(cfg, args):
                                 bits_routed=cfg.bits_routed, bits_shared=cfg.bits_shared,
                                 renorm=True, router=router, gate_vec=gate, experts=pool,
                                 expert_stride=rb, shared_expert=shared))
-    stack = moe.Stack(layers)
+    stack = moe.GdnStack(layers, gdn) if use_gdn else moe.Stack(layers)
     ws = stack.workspace()
     updates = torch.randn(L, H, generator=g, device="cuda").to(torch.bfloat16)
     h = torch.randn(H, generator=g, device="cuda")
     K = cfg.top_k
     idx_log = torch.empty(L, K, dtype=torch.int32, device="cuda")
     w_log = torch.empty(L, K, device="cuda")
-    moe.stack_decode(stack, updates, h, idx_log, w_log, ws)
+    decode = moe.stack_decode_gdn if use_gdn else moe.stack_decode
+    decode(stack, updates, h, idx_log, w_log, ws)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        graph = moe.graph_stack(stack, updates, h, idx_log, w_log, ws, s)
+        if use_gdn:
+            moe.capture_begin(s)
+            decode(stack, updates, h, idx_log, w_log, ws, stream=s)
+            graph = moe.capture_end(s, keep=(stack, updates, h, idx_log, w_log, ws))
+        else:
+            graph = moe.graph_stack(stack, updates, h, idx_log, w_log, ws, s)
     for _ in range(args.warmup):
         graph.launch(s)
     torch.cuda.synchronize()
@@ -256,10 +293,10 @@ def bench_stack(cfg, args):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     assert bool(torch.isfinite(h).all())
-    n_launch = args.profile_passes * L * 4 + 4
+    n_launch = args.profile_passes * L * 7 + 4
     moe.profile_begin(n_launch)
     for _ in range(args.profile_passes):
-        moe.stack_decode(stack, updates, h, idx_log, w_log, ws)
+        decode(stack, updates, h, idx_log, w_log, ws)
     rec = moe.profile_end(n_launch)
     graph.destroy()
     return ms, rec, dict(layers=L, distinct=None)
@@ -712,6 +749,11 @@ def main():
         unit_note = {"stack_us_per_token": round(ms_token * 1000.0, 2),
                      "stack_tokens_per_s": round(1000.0 / ms_token, 2)}
         bytes_per_unit = kb["layer_total"]
+        if cfg.gdn_heads:
+            n_gdn = sum(not synth.is_attention_layer(l) for l in range(cfg.n_layers))
+            tok = cfg.n_layers * kb["layer_total"] + n_gdn * gdn_bytes_per_layer(cfg)
+            bytes_per_unit = tok // cfg.n_layers
+            unit_note.update({"linear_attention_layers": n_gdn, "hbm_bytes_per_token": tok})
     elif cfg.n_tokens > 1:
         ms_call, rec, extra = bench_batch(cfg, args)
         us_per_layer = ms_call * 1000.0
@@ -752,6 +794,9 @@ def main():
                     f"per token over a correlated token stream)",
         "q2_layer": "MoE layer decode, batch 1",
         "q4_stack": f"{cfg.n_layers}-layer resident expert stack, one token (value = per-token time / {cfg.n_layers})",
+        "q4_stack_gdn": f"{cfg.n_layers}-layer resident expert stack whose linear-attention layers open with "
+                        f"their gated-delta-rule block ({cfg.gdn_heads} heads of {cfg.gdn_head_dim}, 4-bit "
+                        f"projections, fp32 state), one token (value = per-token time / {cfg.n_layers})",
         "q4_batch16": f"MoE layer call on {cfg.n_tokens} correlated tokens (value = time per call)",
     }[cfg.name]
     line = {

@@ -80,11 +80,13 @@ bool dim_ok(int d) { return d >= 64 && d <= kMaxDim && d % kGroup == 0; }
 // ---------------------------------------------------------------------------
 struct WsLayout {
   size_t logits, sigma, h_routed, h_shared, y_shared, x_stage, hres_stage, xs_pairs, xs_sums,
-      h_pong, y_routed, g_count, g_expert, g_start, g_pair, ids, rec_src, total;
+      h_pong, y_routed, g_count, g_expert, g_start, g_pair, ids, rec_src, gdn_proj, gdn_o, gdn_h,
+      gdn_const, total;
   size_t xs_pair_stride, xs_sum_stride;  // per token, in u32 / floats
 };
 
-WsLayout ws_layout(const moe_layer_t *L, int T, int n_layers) {
+// gdn_D / gdn_heads: the widest linear-attention block of a stack (0: none)
+WsLayout ws_layout(const moe_layer_t *L, int T, int n_layers, int gdn_D = 0, int gdn_heads = 0) {
   WsLayout w;
   size_t o = 0;
   const size_t E = L->n_experts, K = L->top_k, I = L->inter, H = L->hidden;
@@ -112,6 +114,13 @@ WsLayout ws_layout(const moe_layer_t *L, int T, int n_layers) {
   w.g_pair = o; o += batch ? up256(4 * P) : 0;
   w.ids = o; o += up256(4 * (size_t)kMaxK);  // cache slots of the routed experts (tier path)
   w.rec_src = o; o += up256(16 * (size_t)kMaxK);  // their record addresses and fill targets (tier)
+  // linear-attention blocks of a stack: projections, o, the block's output
+  // and the down/combine launch's constant entry
+  const bool gdn = gdn_D > 0;
+  w.gdn_proj = o; o += gdn ? up256(4 * (3 * (size_t)gdn_D + 2 * (size_t)gdn_heads)) : 0;
+  w.gdn_o = o; o += gdn ? up256(4 * (size_t)gdn_D) : 0;
+  w.gdn_h = o; o += gdn ? up256(4 * H) : 0;
+  w.gdn_const = o; o += gdn ? 256 : 0;
   w.total = o;
   return w;
 }
@@ -723,6 +732,158 @@ int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *up
 }
 
 // ---------------------------------------------------------------------------
+// stacks with linear-attention blocks
+// ---------------------------------------------------------------------------
+static int check_gdn(const moe_layer_t *L, const moe_gdn_layer_t *g, int l) {
+  if (g->n_heads < 1 || (g->d_head != 16 && g->d_head != 32 && g->d_head != 64 && g->d_head != 128 &&
+                         g->d_head != 256))
+    return fail(MOE_EUNSUPPORTED, "layer %d: linear attention needs d_head in {16, 32, 64, 128, 256}, "
+                "n_heads >= 1 (got %d, %d)", l, g->d_head, g->n_heads);
+  const int D = g->n_heads * g->d_head;
+  if (!dim_ok(D)) return fail(MOE_EINVAL, "layer %d: n_heads * d_head = %d: need a multiple of 64 in [64, 8192]", l, D);
+  if (2 * g->n_heads > D) return fail(MOE_EINVAL, "layer %d: 2 n_heads exceeds the gate rows", l);
+  int st;
+  if ((st = check_bits(g->bits, "linear-attention bits")) != MOE_OK) return st;
+  if (!g->rec_qko || !g->rec_vab) return fail(MOE_EINVAL, "layer %d: a projection record is NULL", l);
+  if (!aligned(g->rec_qko, 256) || !aligned(g->rec_vab, 256))
+    return fail(MOE_EALIGN, "layer %d: projection records must be 256-byte aligned", l);
+  if (!aligned(g->state, 16)) return fail(MOE_EALIGN, "layer %d: state must be 16-byte aligned", l);
+  (void)L;
+  return MOE_OK;
+}
+
+static void gdn_extent(const moe_gdn_layer_t *gdn, int n_layers, int &D, int &heads) {
+  D = heads = 0;
+  for (int l = 0; gdn && l < n_layers; ++l) {
+    if (!gdn[l].state) continue;
+    if (gdn[l].n_heads * gdn[l].d_head > D) D = gdn[l].n_heads * gdn[l].d_head;
+    if (gdn[l].n_heads > heads) heads = gdn[l].n_heads;
+  }
+}
+
+// x = RMSNorm(h); projections; the delta-rule step on the layer's state;
+// h_out = h + W_o o (the down/combine kernel with W_o as its one expert)
+static int gdn_block(const moe_layer_t *L, const moe_gdn_layer_t *g, const float *h, float *h_out,
+                     uint8_t *ws, const WsLayout &wl, hipStream_t s) {
+  const int D = g->n_heads * g->d_head;
+  float *proj = reinterpret_cast<float *>(ws + wl.gdn_proj);
+  float *o = reinterpret_cast<float *>(ws + wl.gdn_o);
+  int32_t *one_idx = reinterpret_cast<int32_t *>(ws + wl.gdn_const);
+  float *one_w = reinterpret_cast<float *>(ws + wl.gdn_const) + 1;
+  float *zero_sigma = reinterpret_cast<float *>(ws + wl.gdn_const) + 2;
+  const RecOffsets off = offsets_of(L->hidden, D, g->bits);
+  GdnInParams ip;
+  memset(&ip, 0, sizeof ip);
+  ip.H = L->hidden;
+  ip.D = D;
+  ip.n_heads = g->n_heads;
+  ip.bits = g->bits;
+  ip.h = h;
+  ip.rec_qko = static_cast<const uint8_t *>(g->rec_qko);
+  ip.rec_vab = static_cast<const uint8_t *>(g->rec_vab);
+  ip.off = off;
+  ip.proj = proj;
+  ip.one_idx = one_idx;
+  ip.one_w = one_w;
+  ip.zero_sigma = zero_sigma;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_GDN_IN, [&] { return launch_gdn_in(ip, s); }), "linear-attention projection launch");
+  GdnParams gp;
+  gp.n_sh = g->n_heads;
+  gp.d_k = gp.d_v = g->d_head;
+  gp.q = proj;
+  gp.k = proj + D;
+  gp.v = proj + 2 * D;
+  gp.alpha = proj + 3 * D;
+  gp.beta = proj + 3 * D + g->n_heads;
+  gp.state = g->state;
+  gp.out = o;
+  gp.prep = 1;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_GDN_STEP, [&] { return launch_gdn_step(gp, s); }), "delta-rule step launch");
+  DownParams dp;
+  memset(&dp, 0, sizeof dp);
+  dp.H = L->hidden;
+  dp.I = D;
+  dp.E = 1;
+  dp.bits_r = dp.bits_s = g->bits;
+  dp.experts = static_cast<const uint8_t *>(g->rec_qko);
+  dp.stride = off.total;
+  dp.shared_rec = dp.experts;
+  dp.off = dp.soff = off;
+  dp.combine = 1;
+  dp.idx = one_idx;
+  dp.w = one_w;
+  dp.K = 1;
+  dp.sigma = zero_sigma;
+  dp.h_routed = o;
+  dp.h_shared = nullptr;
+  dp.y = nullptr;
+  dp.h_res = h;
+  dp.out = h_out;
+  dp.shared_ok = 1;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_GDN_OUT, [&] { return launch_down(dp, s); }), "output projection launch");
+  return MOE_OK;
+}
+
+size_t moe_stack_gdn_workspace_bytes(const moe_layer_t *L, const moe_gdn_layer_t *gdn, int n_layers) {
+  if (!L || n_layers < 1) return 0;
+  if (L->top_k < 1 || L->top_k > kMaxK || L->n_experts < 1 || !dim_ok(L->hidden) || !dim_ok(L->inter)) return 0;
+  int D, heads;
+  gdn_extent(gdn, n_layers, D, heads);
+  return ws_layout(L, 1, n_layers, D, heads).total;
+}
+
+int moe_stack_decode_gdn(const moe_layer_t *layers, const moe_gdn_layer_t *gdn, int n_layers,
+                         const uint16_t *updates_bf16, float *h, int32_t *idx_log, float *w_log,
+                         void *ws, size_t ws_bytes, void *stream) {
+  if (!layers || !gdn) return fail(MOE_EINVAL, "layers / gdn is NULL");
+  if (n_layers < 1) return fail(MOE_EINVAL, "n_layers = %d", n_layers);
+  int st;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_layer(&layers[l])) != MOE_OK) return st;
+    const moe_layer_t &a = layers[0], &b = layers[l];
+    if (a.hidden != b.hidden || a.inter != b.inter || a.n_experts != b.n_experts ||
+        a.top_k != b.top_k || a.bits_routed != b.bits_routed || a.bits_shared != b.bits_shared ||
+        a.router_dtype != b.router_dtype || a.gate_dtype != b.gate_dtype)
+      return fail(MOE_EINVAL, "layer %d differs in shape or format from layer 0", l);
+    if (gdn[l].state && (st = check_gdn(&layers[l], &gdn[l], l)) != MOE_OK) return st;
+  }
+  if ((st = check_vec(h, "h")) != MOE_OK) return st;
+  if (updates_bf16 && !aligned(updates_bf16, 16)) return fail(MOE_EALIGN, "updates must be 16-byte aligned");
+  if (!idx_log || !w_log) return fail(MOE_EINVAL, "idx_log / w_log is NULL");
+  if (!aligned(idx_log, 4) || !aligned(w_log, 4)) return fail(MOE_EALIGN, "logs must be 4-byte aligned");
+  const moe_layer_t *L = &layers[0];
+  int D, heads;
+  gdn_extent(gdn, n_layers, D, heads);
+  const WsLayout wl = ws_layout(L, 1, n_layers, D, heads);
+  if ((st = check_ws(ws, ws_bytes, wl.total)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  float *pong = reinterpret_cast<float *>(wsb + wl.h_pong);
+  float *hg = reinterpret_cast<float *>(wsb + wl.gdn_h);
+  const size_t H = L->hidden, K = L->top_k;
+  float *cur = h, *nxt = pong;
+  for (int l = 0; l < n_layers; ++l) {
+    const float *h_in = cur;
+    const uint16_t *u = nullptr;
+    if (gdn[l].state) {
+      if ((st = gdn_block(&layers[l], &gdn[l], cur, hg, wsb, wl, s)) != MOE_OK) return st;
+      h_in = hg;
+    } else if (updates_bf16) {
+      u = updates_bf16 + (size_t)l * H;
+    }
+    st = layer_token(&layers[l], XS_NORM, nullptr, h_in, u, nullptr, nxt, idx_log + l * K,
+                     w_log + l * K, wsb, wl, s);
+    if (st != MOE_OK) return st;
+    float *t = cur;
+    cur = nxt;
+    nxt = t;
+  }
+  if (cur != h)
+    MOE_TRY_HIP(timed(s, MOE_KERNEL_OTHER, [&] { return launch_copy_f32(h, cur, L->hidden, s); }), "copy launch");
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
 // host-memory expert tier: the routed records in page-locked host memory, a
 // cache of n_slots records and the slot table in device memory, all managed
 // on the device (no host round trip, so a token's calls can be captured)
@@ -1011,8 +1172,9 @@ int moe_gdn_step(int n_seq, int n_heads, int d_k, int d_v, const float *q, const
   p.beta = beta;
   p.state = state;
   p.out = out;
+  p.prep = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  MOE_TRY_HIP(timed(s, MOE_KERNEL_OTHER, [&] { return launch_gdn_step(p, s); }), "delta-rule step launch");
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_GDN_STEP, [&] { return launch_gdn_step(p, s); }), "delta-rule step launch");
   return MOE_OK;
 }
 

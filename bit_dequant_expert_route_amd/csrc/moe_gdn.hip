@@ -39,9 +39,17 @@ __global__ __launch_bounds__(kBlock) void k_gdn_step(GdnParams p) {
   const int sh = wave / wph;               // sequence * n_heads + head
   if (sh >= p.n_sh) return;                // wave-uniform
   const int row0 = (wave - sh * wph) * rpw;
-  const float4 k4 = reinterpret_cast<const float4 *>(p.k + (size_t)sh * p.d_k)[li];
-  const float4 q4 = reinterpret_cast<const float4 *>(p.q + (size_t)sh * p.d_k)[li];
-  const float a = p.alpha[sh], b = p.beta[sh];
+  float4 k4 = reinterpret_cast<const float4 *>(p.k + (size_t)sh * p.d_k)[li];
+  float4 q4 = reinterpret_cast<const float4 *>(p.q + (size_t)sh * p.d_k)[li];
+  float a = p.alpha[sh], b = p.beta[sh];
+  if (p.prep) {  // uniform: raw projections and gate logits of the block
+    const float rq = 1.0f / sqrtf(seg_sum(dot4(q4, q4), lg) + 1e-6f);
+    const float rk = 1.0f / sqrtf(seg_sum(dot4(k4, k4), lg) + 1e-6f);
+    q4 = make_float4(q4.x * rq, q4.y * rq, q4.z * rq, q4.w * rq);
+    k4 = make_float4(k4.x * rk, k4.y * rk, k4.z * rk, k4.w * rk);
+    a = 1.0f / (1.0f + expf(-a));
+    b = 1.0f / (1.0f + expf(-b));
+  }
   float *S = p.state + (size_t)sh * p.d_v * p.d_k;
   float4 s4[kGdnPasses];
   float vi[kGdnPasses];
@@ -72,6 +80,123 @@ __global__ __launch_bounds__(kBlock) void k_gdn_step(GdnParams p) {
       if (li == 0) p.out[(size_t)sh * p.d_v + r] = o;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// the block's projections.  Every workgroup normalises h into LDS (two passes:
+// the sum of squares, then the scaled values in the padded chunk layout of
+// the fp32 dot path); each wave takes rows_per_wave rows of one projection
+// matrix and requests them before the normalisation, so that their latency
+// overlaps it.
+// ---------------------------------------------------------------------------
+template <int BITS, int WAVES>
+__device__ __forceinline__ void norm_to_lds(const float *h, int H, float *xl) {
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kSteps = kMaxDim / (4 * kThreads);
+  __shared__ float red[WAVES];
+  float4 hv[kSteps];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int c = (i * kThreads + (int)threadIdx.x) * 4;
+    hv[i] = *reinterpret_cast<const float4 *>(h + (c < H ? c : 0));
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int c = (i * kThreads + (int)threadIdx.x) * 4;
+    if (c < H) {
+      ss = fmaf(hv[i].x, hv[i].x, ss);
+      ss = fmaf(hv[i].y, hv[i].y, ss);
+      ss = fmaf(hv[i].z, hv[i].z, ss);
+      ss = fmaf(hv[i].w, hv[i].w, ss);
+    }
+  }
+  ss = seg_sum(ss, 6);
+  if (lane_id() == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < WAVES; ++i) tot += red[i];
+  const float r = 1.0f / sqrtf(tot / (float)H + 1e-6f);
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int c = (i * kThreads + (int)threadIdx.x) * 4;
+    // H is a multiple of 64, so a chunk's lanes agree on c < H
+    if (c < H)
+      lds_put_chunk4<BITS>(xl, c, make_float4(hv[i].x * r, hv[i].y * r, hv[i].z * r, hv[i].w * r));
+  }
+  __syncthreads();
+}
+
+constexpr int kGdnInWaves = 8;
+
+template <int BITS, int NCH, int NPASS>
+__global__ __launch_bounds__(64 * kGdnInWaves) void k_gdn_in(GdnInParams p) {
+  extern __shared__ float xl[];
+  const int wave = wave_uniform(blockIdx.x * kGdnInWaves + (threadIdx.x >> 6));
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    p.one_idx[0] = 0;
+    p.one_w[0] = 1.0f;
+    p.zero_sigma[0] = 0.0f;
+  }
+  // wave -> matrix (0 q, 1 k, 2 v, 3 the gate rows) and its first row
+  const int rpw = p.rows_per_wave;
+  const int wpm = (p.D + rpw - 1) / rpw;
+  const int mat = wave / wpm < 3 ? wave / wpm : 3;
+  const int row0 = (wave - mat * wpm) * rpw;
+  const int rows = mat < 3 ? p.D : 2 * p.n_heads;
+  const bool active = row0 < rows;
+  RecOffsets o2 = p.off;
+  o2.down_codes = (mat & 1) ? p.off.up_codes : p.off.gate_codes;
+  o2.down_sb = (mat & 1) ? p.off.up_sb : p.off.gate_sb;
+  const uint8_t *rec = mat < 2 ? p.rec_qko : p.rec_vab;
+  const RowMap m = row_map<BITS>(p.H);
+  DnTile<BITS, NCH, NPASS> t;
+  down_load(t, rec, o2, active ? rows : 1, m, active ? row0 : 0);
+  norm_to_lds<BITS, kGdnInWaves>(p.h, p.H, xl);
+  if (!active) return;
+  XStage<BITS, true> xs[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = m.li + (j << m.lg);
+    xs[j] = make_stage<BITS, XS_LDSPAD>(nullptr, xl, c < m.cpr ? c : 0);
+  }
+  float acc[NPASS];
+#pragma unroll
+  for (int i = 0; i < NPASS; ++i) acc[i] = 0.f;
+  down_accumulate_staged<BITS, NCH, NPASS>(xs, m, rows, row0, true, 1.0f, t, acc);
+  float *out = p.proj + (size_t)mat * p.D;
+#pragma unroll
+  for (int i = 0; i < NPASS; ++i) {
+    const float sum = seg_sum(acc[i], m.lg);
+    const int r = row0 + i * m.rpp + m.rip;
+    if (m.li == 0 && r < rows) out[r] = sum;
+  }
+}
+
+hipError_t launch_gdn_in(const GdnInParams &p0, hipStream_t s) {
+  GdnInParams p = p0;
+  const int nch = nch_for(p.H, p.bits);
+  const int rpp = rpp_for(p.H, p.bits);
+  const int npass = clamp_pass(nch, rpp >= 2 ? 1 : 2);
+  p.rows_per_wave = npass * rpp;
+  const int wpm = (p.D + p.rows_per_wave - 1) / p.rows_per_wave;
+  const int waves = 3 * wpm + (2 * p.n_heads + p.rows_per_wave - 1) / p.rows_per_wave;
+  const dim3 grid((waves + kGdnInWaves - 1) / kGdnInWaves);
+  const int nc = 128 / p.bits;
+  const size_t lds = (size_t)(p.H / nc) * (nc + kLdsPad) * sizeof(float);
+#define MOE_GI(BITS)                                                                            \
+  do {                                                                                          \
+    if (nch == 1 && npass == 1) MOE_LAUNCH((k_gdn_in<BITS, 1, 1>), grid, dim3(64 * kGdnInWaves), lds, s, p); \
+    else if (nch == 1) MOE_LAUNCH((k_gdn_in<BITS, 1, 2>), grid, dim3(64 * kGdnInWaves), lds, s, p);          \
+    else if (nch == 2 && npass == 1) MOE_LAUNCH((k_gdn_in<BITS, 2, 1>), grid, dim3(64 * kGdnInWaves), lds, s, p); \
+    else if (nch == 2) MOE_LAUNCH((k_gdn_in<BITS, 2, 2>), grid, dim3(64 * kGdnInWaves), lds, s, p);          \
+    else MOE_LAUNCH((k_gdn_in<BITS, 4, 1>), grid, dim3(64 * kGdnInWaves), lds, s, p);                       \
+  } while (0)
+  if (p.bits == 4) MOE_GI(4);
+  else MOE_GI(2);
+#undef MOE_GI
+  return hipGetLastError();
 }
 
 hipError_t launch_gdn_step(const GdnParams &p, hipStream_t s) {

@@ -283,8 +283,28 @@ struct GdnParams {
   const float *alpha, *beta;      // [n_sh]
   float *state;                   // [n_sh][d_v][d_k], updated in place
   float *out;                     // [n_sh][d_v]
+  // 1: q and k are raw projections, scaled here to unit length per head
+  // (eps 1e-6 under the root), and alpha, beta are logits, made sigmoids here
+  int prep;
 };
 hipError_t launch_gdn_step(const GdnParams &p, hipStream_t s);
+
+// the projections of a linear-attention block: x = RMSNorm(h) formed per
+// workgroup in LDS, then the rows of W_q, W_k (gate, up of rec_qko), W_v and
+// the 2 n_heads gate rows (gate, first rows of up of rec_vab) -> proj
+struct GdnInParams {
+  int H, D, n_heads, bits;
+  const float *h;                 // [H]
+  const uint8_t *rec_qko, *rec_vab;
+  RecOffsets off;                 // record offsets at (H, D, bits)
+  float *proj;                    // [3 D + 2 n_heads]: q, k, v, alpha and beta logits
+  // one routed entry of weight 1 and a zero shared gate, for the output
+  // projection's down/combine launch (written by workgroup 0)
+  int32_t *one_idx;
+  float *one_w, *zero_sigma;
+  int rows_per_wave;              // set by the launcher
+};
+hipError_t launch_gdn_in(const GdnInParams &p, hipStream_t s);
 
 // workspace of moe_layer_decode_noalloc: a device array of this many bytes
 // per GPU (moe_util.hip); *out receives the current device's address of it

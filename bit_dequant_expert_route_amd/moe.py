@@ -42,6 +42,11 @@ class LayerStruct(C.Structure):
     ]
 
 
+class GdnLayerStruct(C.Structure):
+    _fields_ = [("n_heads", C.c_int), ("d_head", C.c_int), ("bits", C.c_int),
+                ("rec_qko", C.c_void_p), ("rec_vab", C.c_void_p), ("state", C.c_void_p)]
+
+
 class WsView(C.Structure):
     _fields_ = [("logits", C.c_void_p), ("sigma", C.c_void_p),
                 ("h_routed", C.c_void_p), ("h_shared", C.c_void_p)]
@@ -70,6 +75,9 @@ def _load():
         "moe_layer_decode_noalloc": (I, [C.POINTER(LayerStruct), I, I, P, P, P, P, P, P]),
         "moe_layer_ws_view": (I, [C.POINTER(LayerStruct), I, P, Z, C.POINTER(WsView)]),
         "moe_stack_decode": (I, [C.POINTER(LayerStruct), I, P, P, P, P, P, Z, P]),
+        "moe_stack_gdn_workspace_bytes": (Z, [C.POINTER(LayerStruct), C.POINTER(GdnLayerStruct), I]),
+        "moe_stack_decode_gdn": (I, [C.POINTER(LayerStruct), C.POINTER(GdnLayerStruct), I, P, P, P,
+                                     P, P, Z, P]),
         "moe_graph_capture_begin": (I, [P]),
         "moe_graph_capture_end": (I, [P, C.POINTER(P)]),
         "moe_graph_create_stack": (I, [C.POINTER(LayerStruct), I, P, P, P, P, P, Z, P, C.POINTER(P)]),
@@ -263,6 +271,35 @@ def stack_decode(stack: Stack, updates, h, idx_log, w_log, ws, stream=None):
                                  _stream(stream)), "moe_stack_decode")
 
 
+class GdnStack:
+    """A stack whose layers may open with a linear-attention block: `gdn[l]`
+    is None for a full-attention layer (its update is used) or a dict with
+    n_heads, d_head, bits and the CUDA tensors rec_qko, rec_vab (projection
+    records) and state ([n_heads][d_head][d_head] fp32, updated in place)."""
+
+    def __init__(self, layers: list[Layer], gdn: list):
+        self.layers, self.gdn = layers, gdn
+        self.arr = (LayerStruct * len(layers))(*[l.s for l in layers])
+        structs = []
+        for g in gdn:
+            if g is None:
+                structs.append(GdnLayerStruct(0, 0, 0, None, None, None))
+            else:
+                structs.append(GdnLayerStruct(g["n_heads"], g["d_head"], g["bits"], _ptr(g["rec_qko"]),
+                                              _ptr(g["rec_vab"]), _ptr(g["state"])))
+        self.garr = (GdnLayerStruct * len(layers))(*structs)
+
+    def workspace(self) -> torch.Tensor:
+        n = int(_lib.moe_stack_gdn_workspace_bytes(C.byref(self.arr[0]), self.garr, len(self.layers)))
+        return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+def stack_decode_gdn(stack: GdnStack, updates, h, idx_log, w_log, ws, stream=None):
+    _check(_lib.moe_stack_decode_gdn(stack.arr, stack.garr, len(stack.layers), _ptr(updates), _ptr(h),
+                                     _ptr(idx_log), _ptr(w_log), _ptr(ws), ws.numel(),
+                                     _stream(stream)), "moe_stack_decode_gdn")
+
+
 class Graph:
     """An instantiated HIP graph (moe_graph_t)."""
 
@@ -312,7 +349,7 @@ def fill_experts(dst, stride: int, n: int, seed: int, layer: int, first_expert: 
 
 
 KERNEL_NAMES = {1: "head", 2: "gateup", 3: "down_combine", 4: "down_y", 5: "topk",
-                6: "combine", 7: "other"}
+                6: "combine", 7: "other", 8: "gdn_in", 9: "gdn_step", 10: "gdn_out"}
 
 
 def profile_begin(max_launches: int):

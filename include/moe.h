@@ -227,6 +227,39 @@ int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *up
                      float *h, int32_t *idx_log, float *w_log,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* One token through a stack whose layers may open with a linear-attention
+ * block ([openclawradar] "Technical implementation": 45 GatedDeltaNet
+ * layers and 15 full-attention layers; "Accelerate BLAS for linear
+ * attention": 64 heads, a 128x128 state each, scale + gemv + rank-1 update;
+ * "Pipeline performance": CMD1 runs the attention projections and the delta
+ * net).  For layer l with gdn[l].state set:
+ *   x = RMSNorm(h); q = W_q x, k = W_k x, v = W_v x (n_heads x d_head each),
+ *   a = W_alpha x, b = W_beta x (one per head); per head q and k scaled to
+ *   unit length (q / sqrt(|q|^2 + 1e-6)), alpha = sigmoid(a), beta =
+ *   sigmoid(b); then S <- alpha S, u = S k, S <- S + beta (v - u) k^T,
+ *   o = S q on the layer's state (updated in place); h <- h + W_o o;
+ * otherwise h <- h + u_l (updates_bf16 row l, skipped when NULL), the stand-in
+ * for a full-attention layer.  Then the MoE layer of moe_stack_decode.  The
+ * projections are quantised matrices in two records of the expert format
+ * with hidden = H and inter = D = n_heads * d_head (moe_expert_bytes(H, D,
+ * bits) bytes each, 256-byte aligned):
+ *   rec_qko: gate = W_q [D][H], up = W_k [D][H], down = W_o [H][D]
+ *   rec_vab: gate = W_v [D][H], up rows 0..n_heads-1 = W_alpha,
+ *            rows n_heads..2 n_heads-1 = W_beta (the other rows unused)
+ * d_head in {16, 32, 64, 128, 256}, D a multiple of 64 up to 8192; state
+ * [n_heads][d_head][d_head] fp32 (row i of a head's state is value i).
+ * ws: moe_stack_gdn_workspace_bytes bytes. */
+typedef struct moe_gdn_layer {
+    int n_heads, d_head, bits;
+    const void *rec_qko;
+    const void *rec_vab;
+    float *state;          /* NULL: a full-attention layer (the update is used) */
+} moe_gdn_layer_t;
+size_t moe_stack_gdn_workspace_bytes(const moe_layer_t *L, const moe_gdn_layer_t *gdn, int n_layers);
+int moe_stack_decode_gdn(const moe_layer_t *layers, const moe_gdn_layer_t *gdn, int n_layers,
+                         const uint16_t *updates_bf16, float *h, int32_t *idx_log, float *w_log,
+                         void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* host-memory expert tier ([openclawradar] "SSD expert streaming",         */
 /* "Pipeline performance" and "Architecture constraint"; [a2a-fr] "Technical */
@@ -307,7 +340,10 @@ enum {
     MOE_KERNEL_DOWN_Y = 4,     /* down projection writing per-expert y */
     MOE_KERNEL_TOPK = 5,
     MOE_KERNEL_COMBINE = 6,
-    MOE_KERNEL_OTHER = 7
+    MOE_KERNEL_OTHER = 7,
+    MOE_KERNEL_GDN_IN = 8,     /* linear-attention block: norm + projections */
+    MOE_KERNEL_GDN_STEP = 9,   /* the gated delta-rule step */
+    MOE_KERNEL_GDN_OUT = 10    /* output projection + residual */
 };
 /* Between moe_profile_begin and moe_profile_end, on the calling thread, every
  * kernel launch of the path entry points records two HIP events through its
