@@ -13,10 +13,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = [os.path.join(CSRC, "moe_kernels.hip"), os.path.join(CSRC, "moe_util.hip"),
-           os.path.join(CSRC, "moe_gdn.hip"), os.path.join(CSRC, "moe_api.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("moe_kernels.hip", "moe_down.hip", "moe_batch.hip",
+                                           "moe_util.hip", "moe_gdn.hip", "moe_api.cpp")]
 HEADERS = [os.path.join(CSRC, "moe_internal.h"), os.path.join(CSRC, "moe_device.h"),
-           os.path.join(CSRC, "moe_sortnet.h"),
+           os.path.join(CSRC, "moe_sortnet.h"), os.path.join(CSRC, "moe_launch.h"),
            os.path.join(os.path.dirname(HERE), "include", "moe.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -80,8 +80,8 @@ bool dim_ok(int d) { return d >= 64 && d <= kMaxDim && d % kGroup == 0; }
 // ---------------------------------------------------------------------------
 struct WsLayout {
   size_t logits, sigma, h_routed, h_shared, y_shared, x_stage, hres_stage, xs_pairs, xs_sums,
-      h_pong, y_routed, g_count, g_expert, g_start, g_pair, ids, rec_src, gdn_proj, gdn_o, gdn_h,
-      gdn_const, total;
+      h_pong, acc, y_routed, g_count, g_expert, g_start, g_pair, ids, rec_src, gdn_proj,
+      gdn_o, gdn_h, gdn_const, total;
   size_t xs_pair_stride, xs_sum_stride;  // per token, in u32 / floats
 };
 
@@ -104,6 +104,8 @@ WsLayout ws_layout(const moe_layer_t *L, int T, int n_layers, int gdn_D = 0, int
   w.xs_pairs = o; o += 4 * w.xs_pair_stride * (size_t)T;
   w.xs_sums = o; o += 4 * w.xs_sum_stride * (size_t)T;
   w.h_pong = o; o += n_layers > 0 ? up256(4 * H) : 0;
+  // stacks: the routing accumulators of the two layer parities
+  w.acc = o; o += n_layers > 0 ? up256(2 * 8 * acc_doubles(L->n_experts)) : 0;
   // token batches: per-pair down outputs and the expert groups
   const size_t P = (size_t)T * K;
   const bool batch = T > 1;
@@ -691,6 +693,23 @@ int moe_layer_ws_view(const moe_layer_t *L, int n_tokens, void *ws, size_t ws_by
   return MOE_OK;
 }
 
+static int stack_run(const moe_layer_t *layers, int n_layers, const uint16_t *updates, float *h,
+                     int32_t *idx_log, float *w_log, uint8_t *ws, const WsLayout &wl, hipStream_t s);
+
+// whether a stack runs with two kernels per layer (stack_run): a shared expert
+// of the routed width (the gate/up launch takes it), and combine launches whose
+// workgroups cover row tiles the routing partials can take; otherwise the
+// layers run as router, gate/up and down/combine kernels.  Stacks with
+// linear-attention blocks keep the router kernel: forming the partials in the
+// block's output projection (rows of 8192 codes, two rounds of workgroups)
+// cost more than the router launch it saves (60-layer stack: 49.3 against
+// 48.4 us per layer).
+static bool stack_two_kernels(const moe_layer_t *layers) {
+  const moe_layer_t &L = layers[0];
+  return L.bits_shared == L.bits_routed &&
+         combine_takes_partials(L.hidden, L.inter, L.bits_routed, L.top_k + 1);
+}
+
 int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *updates_bf16,
                      float *h, int32_t *idx_log, float *w_log, void *ws, size_t ws_bytes,
                      void *stream) {
@@ -714,6 +733,10 @@ int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *up
   if ((st = check_ws(ws, ws_bytes, wl.total)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
+  if (stack_two_kernels(layers))
+    return stack_run(layers, n_layers, updates_bf16, h, idx_log, w_log, wsb, wl, s);
+  // otherwise (a shared expert of another width keeps its gate/up in the
+  // router kernel): three kernels per layer
   float *pong = reinterpret_cast<float *>(wsb + wl.h_pong);
   const size_t H = L->hidden, K = L->top_k;
   float *cur = h, *nxt = pong;
@@ -821,6 +844,128 @@ static int gdn_block(const moe_layer_t *L, const moe_gdn_layer_t *g, const float
   dp.out = h_out;
   dp.shared_ok = 1;
   MOE_TRY_HIP(timed(s, MOE_KERNEL_GDN_OUT, [&] { return launch_down(dp, s); }), "output projection launch");
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// stacks of same-width layers: two kernels per layer.  The down/combine
+// kernel of layer l forms the next layer's input v = out + u_{l+1} and, for
+// its rows, the partial router / gate dots and sum of squares of v
+// (accumulated over workgroups in fp64, spread over kAccCopies copies); the
+// gate/up kernel of layer l + 1 takes its routing and its x = v / rms(v) from
+// those sums.  So no kernel runs between a layer's combine and the next
+// layer's gate/up.  The first layer's sums come from k_partials (or from the
+// output projection of its linear-attention block).
+// ---------------------------------------------------------------------------
+static int stack_gateup(const moe_layer_t *L, const float *v, const double *acc, double *acc_zero,
+                        int32_t *idx, float *w, uint8_t *ws, const WsLayout &wl, hipStream_t s) {
+  GateUpParams gp;
+  memset(&gp, 0, sizeof gp);
+  gp.H = L->hidden;
+  gp.I = L->inter;
+  gp.E = L->n_experts;
+  gp.K = L->top_k;
+  gp.renorm = L->renorm_topk;
+  gp.bits = L->bits_routed;
+  gp.experts = static_cast<const uint8_t *>(L->experts);
+  gp.stride = L->expert_stride;
+  gp.shared_rec = static_cast<const uint8_t *>(L->shared_expert);
+  gp.shared_ok = 1;
+  gp.off = offsets_of(L->hidden, L->inter, L->bits_routed);
+  gp.soff = gp.off;
+  gp.n = L->top_k;
+  gp.idx_out = idx;
+  gp.w_out = w;
+  gp.xsrc = XS_F32;
+  gp.x = v;
+  gp.h_out = reinterpret_cast<float *>(ws + wl.h_routed);
+  gp.with_shared = 1;
+  gp.h_shared_out = reinterpret_cast<float *>(ws + wl.h_shared);
+  gp.acc = acc;
+  gp.acc_zero = acc_zero;
+  gp.acc_zero_n = (int)acc_doubles(L->n_experts);
+  gp.sigma_out = reinterpret_cast<float *>(ws + wl.sigma);
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_GATEUP, [&] { return launch_gateup(gp, s); }), "gate/up launch");
+  return MOE_OK;
+}
+
+static int stack_down(const moe_layer_t *L, const float *v, float *out,
+                      const int32_t *idx, const float *w, const moe_layer_t *next,
+                      const uint16_t *u_next, double *acc_next, uint8_t *ws, const WsLayout &wl,
+                      hipStream_t s) {
+  DownParams dp;
+  memset(&dp, 0, sizeof dp);
+  dp.H = L->hidden;
+  dp.I = L->inter;
+  dp.E = L->n_experts;
+  dp.experts = static_cast<const uint8_t *>(L->experts);
+  dp.stride = L->expert_stride;
+  dp.shared_rec = static_cast<const uint8_t *>(L->shared_expert);
+  dp.off = dp.soff = offsets_of(L->hidden, L->inter, L->bits_routed);
+  dp.shared_ok = 1;
+  dp.combine = 1;
+  dp.bits_r = dp.bits_s = L->bits_routed;
+  dp.idx = idx;
+  dp.w = w;
+  dp.K = L->top_k;
+  dp.sigma = reinterpret_cast<float *>(ws + wl.sigma);  // written by the gate/up launch
+  dp.h_routed = reinterpret_cast<float *>(ws + wl.h_routed);
+  dp.h_shared = reinterpret_cast<float *>(ws + wl.h_shared);
+  dp.h_res = v;
+  dp.out = out;
+  if (next) {
+    dp.nr_router = next->router;
+    dp.nr_router_dtype = next->router_dtype;
+    dp.nr_gate = next->shared_gate;
+    dp.nr_gate_dtype = next->gate_dtype;
+    dp.nr_upd = u_next;
+    dp.nr_acc = acc_next;
+    dp.nr_E = next->n_experts;
+  }
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_DOWN, [&] { return launch_down(dp, s); }), "down/combine launch");
+  return MOE_OK;
+}
+
+// layers share one width and have no linear-attention blocks
+static int stack_run(const moe_layer_t *layers, int n_layers, const uint16_t *updates, float *h,
+                     int32_t *idx_log, float *w_log, uint8_t *ws, const WsLayout &wl, hipStream_t s) {
+  const moe_layer_t *L0 = &layers[0];
+  const size_t H = L0->hidden, K = L0->top_k;
+  const size_t nacc = acc_doubles(L0->n_experts);
+  double *acc[2] = {reinterpret_cast<double *>(ws + wl.acc), reinterpret_cast<double *>(ws + wl.acc) + nacc};
+  float *buf[2] = {h, reinterpret_cast<float *>(ws + wl.h_pong)};
+  auto upd = [&](int l) { return updates ? updates + (size_t)l * H : nullptr; };
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_OTHER, [&] { return launch_zero(acc[0], 2 * nacc * sizeof(double), s); }),
+              "accumulator zero launch");
+  // layer 0's input v = h + u_0 and its routing sums
+  float *v = buf[1];
+  PartialsParams pp;
+  pp.H = (int)H;
+  pp.E = L0->n_experts;
+  pp.h = h;
+  pp.upd = upd(0);
+  pp.v_out = v;
+  pp.router = L0->router;
+  pp.router_dtype = L0->router_dtype;
+  pp.gate = L0->shared_gate;
+  pp.gate_dtype = L0->gate_dtype;
+  pp.acc = acc[0];
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_HEAD, [&] { return launch_partials(pp, s); }), "routing partials launch");
+  int st;
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer_t *Ll = &layers[l];
+    int32_t *idx = idx_log + l * K;
+    float *w = w_log + l * K;
+    if ((st = stack_gateup(Ll, v, acc[l % 2], acc[(l + 1) % 2], idx, w, ws, wl, s)) != MOE_OK) return st;
+    const bool last = l + 1 == n_layers;
+    float *out = v == buf[0] ? buf[1] : buf[0];
+    if ((st = stack_down(Ll, v, out, idx, w, last ? nullptr : &layers[l + 1], last ? nullptr : upd(l + 1),
+                         last ? nullptr : acc[(l + 1) % 2], ws, wl, s)) != MOE_OK)
+      return st;
+    v = out;
+  }
+  if (v != h)
+    MOE_TRY_HIP(timed(s, MOE_KERNEL_OTHER, [&] { return launch_copy_f32(h, v, L0->hidden, s); }), "copy launch");
   return MOE_OK;
 }
 

@@ -441,7 +441,8 @@ __device__ __forceinline__ void xpart_load(XPart<BITS, XS> &xp, const void *x, i
 }
 
 template <int BITS, int XS>
-__device__ __forceinline__ void xpart_store(const XPart<BITS, XS> &xp, uint32_t *xw, int H) {
+__device__ __forceinline__ void xpart_store(const XPart<BITS, XS> &xp, uint32_t *xw, int H,
+                                            float scale = 1.0f) {
   const int t = threadIdx.x;
   if constexpr (XS == XS_BF16) {
     constexpr int NP = ChunkGeom<BITS>::kPairs;
@@ -460,7 +461,8 @@ __device__ __forceinline__ void xpart_store(const XPart<BITS, XS> &xp, uint32_t 
     for (int i = 0; i < XLds<BITS, true>::kF4; ++i) {
       const int col = 4 * (i * kBlock + t);
       // H is a multiple of 64, so a chunk's lanes agree on col < H
-      if (col < H) lds_put_chunk4<BITS>(xl, col, xp.v[i]);
+      const float4 v = xp.v[i];
+      if (col < H) lds_put_chunk4<BITS>(xl, col, make_float4(v.x * scale, v.y * scale, v.z * scale, v.w * scale));
     }
   }
 }
@@ -967,6 +969,134 @@ __device__ __forceinline__ void topk_store(int e, float w, int K, int32_t *idx, 
   if (lane < K) {
     if (idx) idx[lane] = e;
     if (wout) wout[lane] = w;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// routing accumulators of stack layers (kAccCopies copies per entry, fp64)
+// ---------------------------------------------------------------------------
+// fp64 sum of entry e's copies, in copy order
+__device__ __forceinline__ double acc_entry(const double *acc, int E, int e) {
+  const int st = acc_stride(E);
+  double s = 0.0;
+#pragma unroll
+  for (int c = 0; c < kAccCopies; ++c) s += acc[(size_t)c * st + e];
+  return s;
+}
+
+// the norm's reciprocal r = 1 / sqrt(mean(v^2) + 1e-6) from entry E + 1
+__device__ __forceinline__ float acc_rnorm(const double *acc, int E, int H) {
+  return (float)(1.0 / sqrt(acc_entry(acc, E, E + 1) / (double)H + 1e-6));
+}
+
+// the split selection's logits (topk_part_load's layout) from the
+// accumulators: logit = r * dot
+template <int NPL>
+__device__ __forceinline__ void topk_part_load_acc(const double *acc, int E, int w, float r,
+                                                   float (&v)[4]) {
+  const int e0 = (w * 64 + lane_id()) * NPL;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = e0 + i;
+    v[i] = (float)acc_entry(acc, E, e < E ? e : 0) * r;
+  }
+}
+
+// dot of columns [c0, c0 + n) of a router / gate row (fp32 or bf16) with
+// v[0..n) in LDS; n a multiple of 8
+__device__ __forceinline__ float slice_dot(const void *row, int dtype, int c0, int n, const float *v) {
+  float a = 0.f;
+  if (dtype == 1) {
+    const uint4 *w = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(row) + c0);
+    for (int j = 0; j < n / 8; ++j) {
+      const uint4 u = w[j];
+      const float *x = v + 8 * j;
+      a = fmaf(bf_lo(u.x), x[0], a); a = fmaf(bf_hi(u.x), x[1], a);
+      a = fmaf(bf_lo(u.y), x[2], a); a = fmaf(bf_hi(u.y), x[3], a);
+      a = fmaf(bf_lo(u.z), x[4], a); a = fmaf(bf_hi(u.z), x[5], a);
+      a = fmaf(bf_lo(u.w), x[6], a); a = fmaf(bf_hi(u.w), x[7], a);
+    }
+  } else {
+    const float4 *w = reinterpret_cast<const float4 *>(static_cast<const float *>(row) + c0);
+    for (int j = 0; j < n / 4; ++j) {
+      const float4 u = w[j];
+      const float *x = v + 4 * j;
+      a = fmaf(u.x, x[0], a); a = fmaf(u.y, x[1], a);
+      a = fmaf(u.z, x[2], a); a = fmaf(u.w, x[3], a);
+    }
+  }
+  return a;
+}
+
+// the same with the first 64 bytes of the slice already in registers
+__device__ __forceinline__ float slice_dot_pre(const uint4 (&pre)[4], int dtype, int n, const float *v) {
+  float a = 0.f;
+  if (dtype == 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (8 * j < n) {
+        const uint4 u = pre[j];
+        const float *x = v + 8 * j;
+        a = fmaf(bf_lo(u.x), x[0], a); a = fmaf(bf_hi(u.x), x[1], a);
+        a = fmaf(bf_lo(u.y), x[2], a); a = fmaf(bf_hi(u.y), x[3], a);
+        a = fmaf(bf_lo(u.z), x[4], a); a = fmaf(bf_hi(u.z), x[5], a);
+        a = fmaf(bf_lo(u.w), x[6], a); a = fmaf(bf_hi(u.w), x[7], a);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (4 * j < n) {
+        const uint4 u = pre[j];
+        const float *x = v + 4 * j;
+        a = fmaf(__uint_as_float(u.x), x[0], a); a = fmaf(__uint_as_float(u.y), x[1], a);
+        a = fmaf(__uint_as_float(u.z), x[2], a); a = fmaf(__uint_as_float(u.w), x[3], a);
+      }
+    }
+  }
+  return a;
+}
+
+// whether the first 64 bytes hold a whole slice of n columns
+__host__ __device__ __forceinline__ bool slice_fits_pre(int dtype, int n) {
+  return n * (dtype == 1 ? 2 : 4) <= 64;
+}
+
+// request router row e's slice of n columns at column c0 (n * element size
+// <= 64 bytes: slice_fits_pre); nothing past the slice is read
+__device__ __forceinline__ void slice_prefetch(const void *router, int dtype, int H, int e, int c0,
+                                               int n, uint4 (&pre)[4]) {
+  const int esz = dtype == 1 ? 2 : 4;
+  const uint4 *w = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(router) +
+                                                   ((size_t)e * H + c0) * esz);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pre[j] = 16 * j < n * esz ? w[j] : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// One workgroup's routing partials for its rows v[0..n) (LDS), columns
+// [c0, c0 + n): entries e < E the router row dots, E the gate dot, E + 1 the
+// sum of v^2, each added to copy `copy` of acc.  Thread t takes entries t,
+// t + nthreads, ...; pre holds router row t's slice when use_pre, gpre the
+// gate's slice when gate_pre (set only in the thread that takes entry E).
+__device__ __forceinline__ void routing_partials(const void *router, int rdt, const void *gate,
+                                                 int gdt, int E, int H, const float *v, int c0,
+                                                 int n, double *acc, int copy, int nthreads,
+                                                 const uint4 (&pre)[4], bool use_pre,
+                                                 const uint4 (&gpre)[4], bool gate_pre) {
+  const size_t resz = rdt == 1 ? 2 : 4;
+  for (int e = threadIdx.x; e < E + 2; e += nthreads) {
+    float part;
+    if (e < E) {
+      part = (use_pre && e == (int)threadIdx.x)
+                 ? slice_dot_pre(pre, rdt, n, v)
+                 : slice_dot(static_cast<const uint8_t *>(router) + (size_t)e * H * resz, rdt, c0, n, v);
+    } else if (e == E) {
+      part = gate_pre ? slice_dot_pre(gpre, gdt, n, v) : slice_dot(gate, gdt, c0, n, v);
+    } else {
+      part = 0.f;
+      for (int j = 0; j < n; ++j) part = fmaf(v[j], v[j], part);
+    }
+    atomicAdd(acc + (size_t)copy * acc_stride(E) + e, (double)part);
   }
 }
 

@@ -172,6 +172,15 @@ struct GateUpParams {
   // with rec_fill: workgroups after all others copy the down section of every
   // entry that has a fill target (set by the launcher)
   int n_copy_blocks, copy_blocks_per_entry;
+  // stacks: the routing comes from accumulators ([kAccCopies][acc_stride(E)],
+  // see kAccCopies) instead of logits, x is v scaled by the norm's reciprocal
+  // (p.x holds v, fp32), the routed workgroups zero acc_zero (the other
+  // layer parity's accumulators, acc_zero_n doubles), and the first writes
+  // the shared gate's sigmoid to sigma_out
+  const double *acc;
+  double *acc_zero;
+  int acc_zero_n;
+  float *sigma_out;
 };
 hipError_t launch_gateup(const GateUpParams &p, hipStream_t s);
 
@@ -206,8 +215,53 @@ struct DownParams {
   int shared_ok;
   int rows_per_wave;
   int waves_per_expert;           // Y mode
+  // stacks (COMBINE mode): the next layer's routing inputs formed here from
+  // this launch's output rows.  With nr_acc set, the output is
+  // v = out + u_next (u_next may be null) and every workgroup adds, for its
+  // rows, the partial dots of v with each router row and the gate vector and
+  // the partial sum of v^2 into copy (block mod kAccCopies) of nr_acc.
+  const void *nr_router;          // [nr_E][H]
+  int nr_router_dtype;
+  const void *nr_gate;            // [H]
+  int nr_gate_dtype;
+  const uint16_t *nr_upd;         // [H] bf16 or null
+  double *nr_acc;                 // [kAccCopies][acc_stride(nr_E)] or null
+  int nr_E;
 };
 hipError_t launch_down(const DownParams &p, hipStream_t s);
+// whether a combine launch of this shape (n_vectors = K routed + shared) can
+// form the next layer's routing partials (its workgroups stage the SwiGLU
+// outputs in LDS and cover 8..64 rows)
+bool combine_takes_partials(int H, int I, int bits, int n_vectors);
+
+// Routing accumulators of a stack layer: entry e < E the router dot of row e
+// with v, entry E the gate dot, entry E + 1 the sum of v^2; each summed in fp64
+// over kAccCopies copies that the producing workgroups spread their atomic
+// additions over.  The router logits are r * dot and the gate sigmoid's
+// argument r * gate, with r = 1 / sqrt(sum / H + 1e-6).  Copy c is a run of
+// acc_stride(E) doubles (E + 2 rounded up to whole 128-byte lines), so that the
+// lanes of a wave, taking consecutive entries, add into and read consecutive
+// addresses.  Every gate/up workgroup reads all copies, while additions to
+// one address wait on each other: four copies (60-layer q4 stack, per layer:
+// 16 copies 23.1 us, 8 copies 22.0, 4 copies 21.8).
+constexpr int kAccCopies = 4;
+__host__ __device__ constexpr int acc_stride(int E) { return (E + 2 + 15) / 16 * 16; }
+inline size_t acc_doubles(int E) { return (size_t)acc_stride(E) * kAccCopies; }
+
+// the first layer's routing accumulators: v = h + u (written to v_out) and
+// the partial dots of v, from every workgroup's rows
+struct PartialsParams {
+  int H, E;
+  const float *h;
+  const uint16_t *upd;            // [H] bf16 or null
+  float *v_out;
+  const void *router;
+  int router_dtype;
+  const void *gate;
+  int gate_dtype;
+  double *acc;
+};
+hipError_t launch_partials(const PartialsParams &p, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // expert tier: top-K of one token's logits, then each selected expert's cache

@@ -222,7 +222,13 @@ int moe_layer_ws_view(const moe_layer_t *L, int n_tokens, void *ws, size_t ws_by
  *          h <- h + MoE_l(x)   (moe_layer_decode with h_res = h)
  *   h       [H] fp32, read and overwritten
  *   idx_log [n_layers][K], w_log [n_layers][K]: routing of every layer
- * All layers must share hidden/inter/E/K/bits/dtypes with layers[0]. */
+ * All layers must share hidden/inter/E/K/bits/dtypes with layers[0].
+ * With bits_shared == bits_routed the router dots, gate dot and sum of
+ * squares of each layer's input are summed in fp64 from fp32 partials of row
+ * tiles, added in the order the tiles finish: the fp64 sum is exact unless the
+ * partials of one value span more than about 2^22 in magnitude, so a logit can
+ * differ in its last fp32 place between calls only with a chance of about
+ * 2^-29. */
 int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *updates_bf16,
                      float *h, int32_t *idx_log, float *w_log,
                      void *ws, size_t ws_bytes, void *stream);
