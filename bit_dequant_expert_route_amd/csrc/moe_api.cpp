@@ -154,8 +154,8 @@ int check_layer(const moe_layer_t *L) {
   if (L->renorm_topk != 0 && L->renorm_topk != 1) return fail(MOE_EINVAL, "renorm_topk must be 0 or 1");
   if (!L->router || !L->shared_gate || !L->experts || !L->shared_expert)
     return fail(MOE_EINVAL, "a weight pointer of the layer is NULL");
-  if (!aligned(L->router, 16) || !aligned(L->shared_gate, 16))
-    return fail(MOE_EALIGN, "router and shared_gate must be 16-byte aligned");
+  if (!aligned(L->router, 16) || !aligned(L->shared_gate, 16) || !aligned(L->router_tiles, 16))
+    return fail(MOE_EALIGN, "router, router_tiles and shared_gate must be 16-byte aligned");
   if (!aligned(L->experts, 256) || !aligned(L->shared_expert, 256) || L->expert_stride % 256)
     return fail(MOE_EALIGN, "expert records and expert_stride must be 256-byte aligned");
   const size_t rb = moe_expert_bytes(L->hidden, L->inter, L->bits_routed, L->group);
@@ -412,7 +412,7 @@ const char *moe_strerror(int status) {
 
 const char *moe_last_error(void) { return g_err; }
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 size_t moe_qmatrix_bytes(int rows, int cols, int bits, int group) {
   if (group != kGroup || (bits != 4 && bits != 2) || rows < 1 || cols < kGroup || cols % kGroup) return 0;
@@ -754,6 +754,24 @@ int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *up
   return MOE_OK;
 }
 
+int moe_router_tile(const void *router, int n_experts, int hidden, moe_dtype router_dtype,
+                    void *out, void *stream) {
+  int st;
+  if ((st = check_dtype(router_dtype, "router_dtype")) != MOE_OK) return st;
+  if (n_experts < 1 || n_experts > kMaxE) return fail(MOE_EINVAL, "n_experts = %d: need 1..1024", n_experts);
+  if (!dim_ok(hidden)) return fail(MOE_EINVAL, "hidden = %d: need a multiple of 64 in [64, 8192]", hidden);
+  if ((st = check_vec(router, "router")) != MOE_OK) return st;
+  if ((st = check_vec(out, "out")) != MOE_OK) return st;
+  const size_t esz = router_dtype == MOE_BF16 ? 2 : 4;
+  const size_t bytes = (size_t)n_experts * hidden * esz;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(router), b = reinterpret_cast<uintptr_t>(out);
+  if (a < b + bytes && b < a + bytes) return fail(MOE_EINVAL, "out overlaps router");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_OTHER, [&] { return launch_router_tile(router, n_experts, hidden, (int)esz, out, s); }),
+              "router tile launch");
+  return MOE_OK;
+}
+
 // ---------------------------------------------------------------------------
 // stacks with linear-attention blocks
 // ---------------------------------------------------------------------------
@@ -915,6 +933,7 @@ static int stack_down(const moe_layer_t *L, const float *v, float *out,
   dp.out = out;
   if (next) {
     dp.nr_router = next->router;
+    dp.nr_router_tiles = next->router_tiles;
     dp.nr_router_dtype = next->router_dtype;
     dp.nr_gate = next->shared_gate;
     dp.nr_gate_dtype = next->gate_dtype;
@@ -946,6 +965,7 @@ static int stack_run(const moe_layer_t *layers, int n_layers, const uint16_t *up
   pp.upd = upd(0);
   pp.v_out = v;
   pp.router = L0->router;
+  pp.router_tiles = L0->router_tiles;
   pp.router_dtype = L0->router_dtype;
   pp.gate = L0->shared_gate;
   pp.gate_dtype = L0->gate_dtype;

@@ -1073,6 +1073,23 @@ __device__ __forceinline__ void slice_prefetch(const void *router, int dtype, in
   for (int j = 0; j < 4; ++j) pre[j] = 16 * j < n * esz ? w[j] : make_uint4(0u, 0u, 0u, 0u);
 }
 
+// the same slice from the column tiles of the router (moe_router_tile: tile t
+// holds columns 8t..8t+7 of every expert, 8 * element size bytes each); c0 a
+// multiple of 8.  Fills pre exactly as slice_prefetch does.
+__device__ __forceinline__ void slice_prefetch_tiles(const void *tiles, int dtype, int E, int e, int c0,
+                                                     int n, uint4 (&pre)[4]) {
+  const uint4 *w = static_cast<const uint4 *>(tiles);
+  const int t0 = c0 / 8;
+  if (dtype == 1) {  // one 16-byte run per tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pre[j] = 16 * j < n * 2 ? w[(size_t)(t0 + j) * E + e] : make_uint4(0u, 0u, 0u, 0u);
+  } else {           // two 16-byte halves per tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      pre[j] = 16 * j < n * 4 ? w[((size_t)(t0 + j / 2) * E + e) * 2 + (j & 1)] : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
 // One workgroup's routing partials for its rows v[0..n) (LDS), columns
 // [c0, c0 + n): entries e < E the router row dots, E the gate dot, E + 1 the
 // sum of v^2, each added to copy `copy` of acc.  Thread t takes entries t,

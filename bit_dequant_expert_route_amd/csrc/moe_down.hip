@@ -54,7 +54,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_down_combine(DownParams p) {
   const int wg_row0 = blk * wg_rows;
   uint4 rpre[4], gpre[4] = {};
   const bool use_pre = epi && slice_fits_pre(p.nr_router_dtype, wg_rows) && (int)threadIdx.x < p.nr_E;
-  if (use_pre) slice_prefetch(p.nr_router, p.nr_router_dtype, p.H, threadIdx.x, wg_row0, wg_rows, rpre);
+  if (use_pre) {
+    if (p.nr_router_tiles)
+      slice_prefetch_tiles(p.nr_router_tiles, p.nr_router_dtype, p.nr_E, threadIdx.x, wg_row0, wg_rows, rpre);
+    else
+      slice_prefetch(p.nr_router, p.nr_router_dtype, p.H, threadIdx.x, wg_row0, wg_rows, rpre);
+  }
   const bool gate_pre = epi && slice_fits_pre(p.nr_gate_dtype, wg_rows) && (int)threadIdx.x == p.nr_E % kThreads;
   if (gate_pre) slice_prefetch(p.nr_gate, p.nr_gate_dtype, p.H, 0, wg_row0, wg_rows, gpre);
   // experts in order: the shared one (if here), then the routed ones
@@ -228,7 +233,12 @@ __global__ __launch_bounds__(kBlock) void k_partials(PartialsParams p) {
   const int r0 = blockIdx.x * kPartialsRows;
   uint4 rpre[4];
   const bool use_pre = slice_fits_pre(p.router_dtype, kPartialsRows) && (int)threadIdx.x < p.E;
-  if (use_pre) slice_prefetch(p.router, p.router_dtype, p.H, threadIdx.x, r0, kPartialsRows, rpre);
+  if (use_pre) {
+    if (p.router_tiles)
+      slice_prefetch_tiles(p.router_tiles, p.router_dtype, p.E, threadIdx.x, r0, kPartialsRows, rpre);
+    else
+      slice_prefetch(p.router, p.router_dtype, p.H, threadIdx.x, r0, kPartialsRows, rpre);
+  }
   uint4 gpre[4] = {};
   const bool gate_pre = slice_fits_pre(p.gate_dtype, kPartialsRows) && (int)threadIdx.x == p.E % kBlock;
   if (gate_pre) slice_prefetch(p.gate, p.gate_dtype, p.H, 0, r0, kPartialsRows, gpre);

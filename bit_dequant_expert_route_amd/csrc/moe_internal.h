@@ -221,6 +221,7 @@ struct DownParams {
   // rows, the partial dots of v with each router row and the gate vector and
   // the partial sum of v^2 into copy (block mod kAccCopies) of nr_acc.
   const void *nr_router;          // [nr_E][H]
+  const void *nr_router_tiles;    // the same in column tiles (moe_router_tile) or null
   int nr_router_dtype;
   const void *nr_gate;            // [H]
   int nr_gate_dtype;
@@ -256,12 +257,16 @@ struct PartialsParams {
   const uint16_t *upd;            // [H] bf16 or null
   float *v_out;
   const void *router;
+  const void *router_tiles;       // column tiles (moe_router_tile) or null
   int router_dtype;
   const void *gate;
   int gate_dtype;
   double *acc;
 };
 hipError_t launch_partials(const PartialsParams &p, hipStream_t s);
+
+// out[t][e][0..8) = router[e][8t..8t+8) (element size esz)
+hipError_t launch_router_tile(const void *router, int E, int H, int esz, void *out, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // expert tier: top-K of one token's logits, then each selected expert's cache

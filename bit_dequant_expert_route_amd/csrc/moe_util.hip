@@ -1,5 +1,5 @@
 // moe_util.hip -- kernels around the hot path: the stand-alone combine, the
-// seeded synthetic-weight fill, zeroing and a copy.
+// seeded synthetic-weight fill, the router's column tiles, zeroing and a copy.
 #include "moe_internal.h"
 
 #include <stdint.h>
@@ -147,9 +147,31 @@ __global__ __launch_bounds__(kBlock) void k_copy_f32(float *dst, const float *sr
   if (i < n) dst[i] = src[i];
 }
 
+// router column tiles: thread i copies the 8 columns of expert e = i mod E in
+// tile t = i / E (8 * esz bytes, as 16-byte words)
+__global__ __launch_bounds__(kBlock) void k_router_tile(const uint8_t *router, int E, int H, int esz,
+                                                        uint8_t *out) {
+  const size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+  const size_t n = (size_t)E * (H / 8);
+  if (i >= n) return;
+  const int e = (int)(i % E);
+  const size_t t = i / E;
+  const uint4 *src = reinterpret_cast<const uint4 *>(router + ((size_t)e * H + t * 8) * esz);
+  uint4 *dst = reinterpret_cast<uint4 *>(out + i * 8 * esz);
+  for (int w = 0; w < esz / 2; ++w) dst[w] = src[w];
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+hipError_t launch_router_tile(const void *router, int E, int H, int esz, void *out, hipStream_t s) {
+  const size_t n = (size_t)E * (H / 8);
+  if (n == 0) return hipSuccess;
+  MOE_LAUNCH(k_router_tile, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+             static_cast<const uint8_t *>(router), E, H, esz, static_cast<uint8_t *>(out));
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineParams &p, hipStream_t s) {
   MOE_LAUNCH(k_combine, dim3((p.H + kBlock - 1) / kBlock), dim3(kBlock), 0, s, p);
   return hipGetLastError();

@@ -38,7 +38,7 @@ class LayerStruct(C.Structure):
         ("router_dtype", C.c_int), ("router", C.c_void_p),
         ("gate_dtype", C.c_int), ("shared_gate", C.c_void_p),
         ("experts", C.c_void_p), ("expert_stride", C.c_size_t),
-        ("shared_expert", C.c_void_p),
+        ("shared_expert", C.c_void_p), ("router_tiles", C.c_void_p),
     ]
 
 
@@ -75,6 +75,7 @@ def _load():
         "moe_layer_decode_noalloc": (I, [C.POINTER(LayerStruct), I, I, P, P, P, P, P, P]),
         "moe_layer_ws_view": (I, [C.POINTER(LayerStruct), I, P, Z, C.POINTER(WsView)]),
         "moe_stack_decode": (I, [C.POINTER(LayerStruct), I, P, P, P, P, P, Z, P]),
+        "moe_router_tile": (I, [P, I, I, I, P, P]),
         "moe_stack_gdn_workspace_bytes": (Z, [C.POINTER(LayerStruct), C.POINTER(GdnLayerStruct), I]),
         "moe_stack_decode_gdn": (I, [C.POINTER(LayerStruct), C.POINTER(GdnLayerStruct), I, P, P, P,
                                      P, P, Z, P]),
@@ -167,13 +168,24 @@ class Layer:
     """A MoE layer's shapes and weights (torch CUDA tensors it keeps alive)."""
 
     def __init__(self, *, hidden, inter, n_experts, top_k, bits_routed, bits_shared,
-                 renorm, router, gate_vec, experts, expert_stride, shared_expert):
+                 renorm, router, gate_vec, experts, expert_stride, shared_expert,
+                 router_tiles=None):
         self.router, self.gate_vec = router, gate_vec
         self.experts, self.shared_expert = experts, shared_expert
+        self.router_tiles = router_tiles
         self.s = LayerStruct(hidden, inter, n_experts, top_k, GROUP, bits_routed, bits_shared,
                              int(renorm), _dtype_code(router), _ptr(router),
                              _dtype_code(gate_vec), _ptr(gate_vec),
-                             _ptr(experts), expert_stride, _ptr(shared_expert))
+                             _ptr(experts), expert_stride, _ptr(shared_expert),
+                             _ptr(router_tiles))
+
+    def with_router_tiles(self, stream=None) -> "Layer":
+        """This layer with its router's column tiles (moe_router_tile), which
+        stacks read to form the routing sums."""
+        if self.router_tiles is None:
+            self.router_tiles = router_tile(self.router, self.s.n_experts, self.s.hidden, stream=stream)
+            self.s.router_tiles = _ptr(self.router_tiles)
+        return self
 
     def __getattr__(self, name):
         s = self.__dict__.get("s")
@@ -186,6 +198,15 @@ class Layer:
 
     def workspace(self, n_tokens: int = 1) -> torch.Tensor:
         return torch.empty(self.workspace_bytes(n_tokens), dtype=torch.uint8, device="cuda")
+
+
+def router_tile(router, n_experts=None, hidden=None, stream=None):
+    """moe_router_tile: the [E][H] router as [H/8][E][8] column tiles."""
+    E, H = (n_experts, hidden) if n_experts is not None else router.shape
+    out = torch.empty(H // 8, E, 8, dtype=router.dtype, device=router.device)
+    _check(_lib.moe_router_tile(_ptr(router), E, H, _dtype_code(router), _ptr(out), _stream(stream)),
+           "moe_router_tile")
+    return out
 
 
 def _ws(layer: Layer, ws, n_tokens: int):
@@ -254,11 +275,20 @@ def ws_view(layer: Layer, n_tokens: int, ws) -> dict:
 
 
 class Stack:
-    """Layers of one resident expert stack (all shaped like layers[0])."""
+    """Layers of one resident expert stack (all shaped like layers[0]); with
+    router_tiles (the default) each layer gets its router's column tiles."""
 
-    def __init__(self, layers: list[Layer]):
+    def __init__(self, layers: list[Layer], router_tiles: bool = True):
+        structs = []
+        for l in layers:
+            if router_tiles:
+                l.with_router_tiles()
+            st = LayerStruct.from_buffer_copy(l.s)
+            if not router_tiles:
+                st.router_tiles = None
+            structs.append(st)
         self.layers = layers
-        self.arr = (LayerStruct * len(layers))(*[l.s for l in layers])
+        self.arr = (LayerStruct * len(layers))(*structs)
 
     def workspace(self) -> torch.Tensor:
         n = int(_lib.moe_stack_workspace_bytes(C.byref(self.arr[0]), len(self.layers)))

@@ -94,6 +94,10 @@ typedef struct moe_layer {
     const void *experts;       /* E routed records, `expert_stride` bytes apart */
     size_t expert_stride;
     const void *shared_expert; /* one record at bits_shared */
+    const void *router_tiles;  /* optional (may be NULL): the router re-laid by
+                                  moe_router_tile; stacks then read it to form
+                                  each layer's routing sums (same values,
+                                  coalesced reads).  16-byte aligned. */
 } moe_layer_t;
 
 /* ---------------------------------------------------------------------- */
@@ -232,6 +236,18 @@ int moe_layer_ws_view(const moe_layer_t *L, int n_tokens, void *ws, size_t ws_by
 int moe_stack_decode(const moe_layer_t *layers, int n_layers, const uint16_t *updates_bf16,
                      float *h, int32_t *idx_log, float *w_log,
                      void *ws, size_t ws_bytes, void *stream);
+
+/* The router [E][H] (dtype router_dtype) re-laid for stacks as column tiles:
+ * out[t][e][j] = router[e][8 t + j] for t < H / 8, j < 8, so that the eight
+ * columns of every expert in a tile are one 16-byte (bf16) or 32-byte (fp32)
+ * run and the experts of a tile are consecutive.  A stack layer's combine
+ * reads, for its rows, one such run per expert of the next layer: the router
+ * slices of [openclawradar] "Pipeline performance" CMD3 (combine + norm
+ * feeding the next layer's routing), read without strided row accesses.
+ * out: E * H * element bytes, 16-byte aligned, caller-owned, not aliasing
+ * router.  H must be a multiple of 64.  Enqueued on `stream`. */
+int moe_router_tile(const void *router, int n_experts, int hidden, moe_dtype router_dtype,
+                    void *out, void *stream);
 
 /* One token through a stack whose layers may open with a linear-attention
  * block ([openclawradar] "Technical implementation": 45 GatedDeltaNet

@@ -30,7 +30,7 @@ def test_sizes():
         lay = synth.record_layout(H, I, b)
         assert moe.expert_offsets(H, I, b) == [lay.gate_codes, lay.up_codes, lay.down_codes,
                                               lay.gate_sb, lay.up_sb, lay.down_sb]
-    assert moe.lib.moe_abi_version() == 1
+    assert moe.lib.moe_abi_version() == 2
     for s in (0, -1, -2, -3, -4, -5):
         assert moe.lib.moe_strerror(s)
 
@@ -72,6 +72,7 @@ def _err():
     (dict(router=0), moe.MOE_EINVAL),
     (dict(experts=0), moe.MOE_EINVAL),
     (dict(router=0x100004), moe.MOE_EALIGN),
+    (dict(router_tiles=0x100008), moe.MOE_EALIGN),
     (dict(experts=0x10000010), moe.MOE_EALIGN),
     (dict(expert_stride=7077888 + 16), moe.MOE_EALIGN),
     (dict(expert_stride=7077888 - 256), moe.MOE_EINVAL),
@@ -157,3 +158,16 @@ def test_noalloc_refuses_a_workspace_beyond_its_scratch():
     st = moe.lib.moe_layer_decode_noalloc(C.byref(_layer(group=32)), 1, 1, 0x500000, 0x600000,
                                           0x700000, 0x800000, 0x900000, None)
     assert st == moe.MOE_EUNSUPPORTED
+
+
+def test_router_tile_validates():
+    f = moe.lib.moe_router_tile
+    R, O = 0x1000000, 0x2000000
+    assert f(0, 512, 4096, 1, O, None) == moe.MOE_EINVAL
+    assert f(R, 512, 4096, 1, 0, None) == moe.MOE_EINVAL
+    assert f(R + 8, 512, 4096, 1, O, None) == moe.MOE_EALIGN
+    assert f(R, 512, 4096, 7, O, None) == moe.MOE_EUNSUPPORTED
+    assert f(R, 0, 4096, 1, O, None) == moe.MOE_EINVAL
+    assert f(R, 512, 100, 1, O, None) == moe.MOE_EINVAL
+    assert f(R, 512, 4096, 1, R + 4096, None) == moe.MOE_EINVAL  # out overlaps router
+    assert "overlaps" in _err()

@@ -2,7 +2,8 @@
 x = RMSNorm(h) in fp32, then the layer) against the oracle walking the same
 layers in fp64.  Per layer the selected experts must match as a set and their
 weights per index; the final residual stream and each layer's weights meet
-err_metric <= 2e-3."""
+err_metric <= 2e-3.  The router's column tiles (moe_router_tile) must give the
+same stack output bit for bit as reading the router rows."""
 import numpy as np
 import pytest
 import torch
@@ -34,7 +35,7 @@ def _build(cfg, case):
                                 experts=pool, expert_stride=rb, shared_expert=shared))
     stack = moe.Stack(layers)
     updates = to_dev(case.updates.astype(np.uint16).view(np.int16)).view(torch.bfloat16)
-    return stack, updates
+    return stack, updates, layers
 
 
 def _check(case, h, idx_log, w_log):
@@ -50,11 +51,11 @@ def _check(case, h, idx_log, w_log):
     return e
 
 
-def _run(cfg, seed, n_layers=None, graph_replays=0):
+def _run(cfg, seed, n_layers=None, graph_replays=0, rows_too=False):
     from bit_dequant_expert_route_amd import moe
     case = make_stack_case(cfg, seed, n_layers)
     log(f"stack {cfg.name} seed {seed}: {case.n_layers} layers, update redraws {sum(case.attempts)}")
-    stack, updates = _build(cfg, case)
+    stack, updates, layers = _build(cfg, case)
     ws = stack.workspace()
     K, L = cfg.top_k, case.n_layers
     h = to_dev(case.h0)
@@ -65,6 +66,13 @@ def _run(cfg, seed, n_layers=None, graph_replays=0):
     eager = h.cpu().numpy()
     err = _check(case, eager, idx_log.cpu().numpy(), w_log.cpu().numpy())
     log(f"  eager: err(h) {err:.2e}")
+    if rows_too:  # the same stack reading the router rows instead of its tiles
+        rows = moe.Stack(layers, router_tiles=False)
+        h_rows = to_dev(case.h0)
+        moe.stack_decode(rows, updates, h_rows, idx_log, w_log, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(h_rows.cpu().numpy(), eager), "router rows and tiles differ"
+        log("  router rows give the tiles' output bit for bit")
     if graph_replays:
         s = torch.cuda.Stream()
         h0 = to_dev(case.h0)
@@ -86,7 +94,7 @@ def _run(cfg, seed, n_layers=None, graph_replays=0):
 
 @pytest.mark.parametrize("seed", [3, 11])
 def test_tiny_stack(seed):
-    _run(synth.CONFIGS["tiny_stack"], seed, graph_replays=3 if seed == 3 else 0)
+    _run(synth.CONFIGS["tiny_stack"], seed, graph_replays=3 if seed == 3 else 0, rows_too=True)
 
 
 @pytest.mark.parametrize("seed", [3, 23])
@@ -100,7 +108,7 @@ def test_q4_stack_60_layers(seed):
     need = cfg.n_layers * (cfg.n_experts * cfg.record_bytes + cfg.shared_record_bytes) + (4 << 30)
     if free < need:
         pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory, {free / 2**30:.0f} GiB free")
-    _run(cfg, seed, graph_replays=1 if seed == 3 else 0)
+    _run(cfg, seed, graph_replays=1 if seed == 3 else 0, rows_too=seed == 3)
 
 
 STACK_EDGE = {
@@ -115,4 +123,18 @@ STACK_EDGE = {
 
 @pytest.mark.parametrize("name", list(STACK_EDGE))
 def test_stack_edges(name):
-    _run(STACK_EDGE[name], 13, graph_replays=1)
+    _run(STACK_EDGE[name], 13, graph_replays=1, rows_too=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_router_tile_layout(dtype):
+    """moe_router_tile: tile t, expert e holds columns 8t..8t+7 of row e."""
+    from bit_dequant_expert_route_amd import moe
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    E, H = 48, 192
+    r = torch.randn(E, H, generator=g, device="cuda").to(dtype)
+    t = moe.router_tile(r)
+    torch.cuda.synchronize()
+    want = r.cpu().reshape(E, H // 8, 8).permute(1, 0, 2).contiguous()
+    assert torch.equal(t.cpu(), want)
