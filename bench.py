@@ -37,10 +37,10 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", "--iters", dest="steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--instances", type=int, default=128)
-    ap.add_argument("--workload", default="q4_layer",
+    ap.add_argument("--workload", "--config", dest="workload", default="q4_layer",
                     choices=["q4_layer", "q2_layer", "q4_stack", "q4_stack_gdn", "q4_batch16", "gdn_step",
                              "q4_tier"])
     ap.add_argument("--tier-slots", type=int, default=128,
@@ -57,7 +57,39 @@ def parse():
     ap.add_argument("--profile-passes", type=int, default=3)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (counter scaling for rocprofv3 --pmc)")
-    return ap.parse_args()
+    ap.add_argument("--seed", type=int, default=0,
+                    help="offset added to every seed of the synthetic weights and activations")
+    ap.add_argument("--bits", type=int, choices=[2, 4], default=None,
+                    help="width of routed and shared experts (default: the workload's)")
+    ap.add_argument("--renorm", type=int, choices=[0, 1], default=1,
+                    help="1: the K selected probabilities are renormalised to sum 1")
+    ap.add_argument("--x-dtype", choices=["bf16", "f32"], default=None,
+                    help="single-layer workloads: dtype of the layer input x (default: the workload's)")
+    args = ap.parse_args()
+    OPTS.update(seed=args.seed, renorm=bool(args.renorm))
+    return args
+
+
+# options the weight and input builders read (set from the command line)
+OPTS = {"seed": 0, "renorm": True}
+
+
+def workload_config(args):
+    """The named workload's configuration with the command line's overrides
+    (--bits, --x-dtype); an overridden workload gets a name that says so."""
+    import dataclasses
+    from bit_dequant_expert_route_amd import synth
+    cfg = synth.CONFIGS["q4_layer" if args.workload == "q4_tier" else args.workload]
+    over, tags = {}, []
+    if args.bits and (args.bits != cfg.bits_routed or args.bits != cfg.bits_shared):
+        over.update(bits_routed=args.bits, bits_shared=args.bits)
+        tags.append(f"bits{args.bits}")
+    if args.x_dtype and args.x_dtype != cfg.x_dtype:
+        over["x_dtype"] = args.x_dtype
+        tags.append(f"x{args.x_dtype}")
+    if not over:
+        return cfg
+    return dataclasses.replace(cfg, name=cfg.name + "+" + "+".join(tags), **over)
 
 
 def kernel_bytes(cfg):
@@ -122,6 +154,7 @@ def valu_from_profiles(workload, kernel, live_us):
 
 
 def build_rotation(cfg, R, seed0=1000):
+    seed0 += OPTS["seed"]
     import torch
     from bit_dequant_expert_route_amd import moe, synth
     H, I, E = cfg.hidden, cfg.inter, cfg.n_experts
@@ -140,10 +173,11 @@ def build_rotation(cfg, R, seed0=1000):
         router = (torch.randn(E, H, generator=g, device="cuda") * synth.ROUTER_STD).to(torch.bfloat16)
         gate = (torch.randn(H, generator=g, device="cuda") * synth.GATEVEC_STD).to(torch.bfloat16)
         h = torch.randn(H, generator=g, device="cuda")
-        x = (h / torch.sqrt(torch.mean(h * h) + 1e-6)).to(torch.bfloat16)
+        x = h / torch.sqrt(torch.mean(h * h) + 1e-6)
+        x = x.to(torch.bfloat16) if cfg.x_dtype == "bf16" else x
         layers.append(moe.Layer(hidden=H, inter=I, n_experts=E, top_k=cfg.top_k,
                                 bits_routed=cfg.bits_routed, bits_shared=cfg.bits_shared,
-                                renorm=True, router=router, gate_vec=gate, experts=pool,
+                                renorm=OPTS["renorm"], router=router, gate_vec=gate, experts=pool,
                                 expert_stride=rb, shared_expert=shared[i * sb:(i + 1) * sb]))
         xs.append(x)
         hres.append(h)
@@ -234,7 +268,8 @@ def bench_stack(cfg, args):
     rb = synth.record_layout(H, I, cfg.bits_routed).total
     sb = synth.record_layout(H, I, cfg.bits_shared).total
     g = torch.Generator(device="cuda")
-    g.manual_seed(3000)
+    S = 3000 + OPTS["seed"]
+    g.manual_seed(S)
     layers, keep, gdn = [], [], []
     use_gdn = cfg.gdn_heads > 0
     D = cfg.gdn_heads * cfg.gdn_head_dim
@@ -244,7 +279,7 @@ def bench_stack(cfg, args):
             recs = []
             for gid in (synth.GDN_QKO_GEN_ID, synth.GDN_VAB_GEN_ID):
                 r = torch.empty(gb, dtype=torch.uint8, device="cuda")
-                moe.fill_experts(r, gb, 1, 3000, l, gid, H, D, cfg.gdn_bits,
+                moe.fill_experts(r, gb, 1, S, l, gid, H, D, cfg.gdn_bits,
                                  synth.dist_for_bits(cfg.gdn_bits))
                 recs.append(r)
             st = torch.randn(cfg.gdn_heads, cfg.gdn_head_dim, cfg.gdn_head_dim, generator=g,
@@ -254,15 +289,15 @@ def bench_stack(cfg, args):
         else:
             gdn.append(None)
         pool = torch.empty(E * rb, dtype=torch.uint8, device="cuda")
-        moe.fill_experts(pool, rb, E, 3000, l, 0, H, I, cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
+        moe.fill_experts(pool, rb, E, S, l, 0, H, I, cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
         shared = torch.empty(sb, dtype=torch.uint8, device="cuda")
-        moe.fill_experts(shared, sb, 1, 3000, l, synth.SHARED_GEN_ID, H, I, cfg.bits_shared,
+        moe.fill_experts(shared, sb, 1, S, l, synth.SHARED_GEN_ID, H, I, cfg.bits_shared,
                          synth.dist_for_bits(cfg.bits_shared))
         router = (torch.randn(E, H, generator=g, device="cuda") * synth.ROUTER_STD).to(torch.bfloat16)
         gate = (torch.randn(H, generator=g, device="cuda") * synth.GATEVEC_STD).to(torch.bfloat16)
         layers.append(moe.Layer(hidden=H, inter=I, n_experts=E, top_k=cfg.top_k,
                                 bits_routed=cfg.bits_routed, bits_shared=cfg.bits_shared,
-                                renorm=True, router=router, gate_vec=gate, experts=pool,
+                                renorm=OPTS["renorm"], router=router, gate_vec=gate, experts=pool,
                                 expert_stride=rb, shared_expert=shared))
     stack = moe.GdnStack(layers, gdn) if use_gdn else moe.Stack(layers)
     ws = stack.workspace()
@@ -349,12 +384,13 @@ def bench_batch(cfg, args):
     rb = synth.record_layout(H, I, cfg.bits_routed).total
     sb = synth.record_layout(H, I, cfg.bits_shared).total
     pool = torch.empty(E * rb, dtype=torch.uint8, device="cuda")
-    moe.fill_experts(pool, rb, E, 4000, 0, 0, H, I, cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
+    S = 4000 + OPTS["seed"]
+    moe.fill_experts(pool, rb, E, S, 0, 0, H, I, cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
     shared = torch.empty(R * sb, dtype=torch.uint8, device="cuda")
-    moe.fill_experts(shared, sb, R, 4000, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared,
+    moe.fill_experts(shared, sb, R, S, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared,
                      synth.dist_for_bits(cfg.bits_shared))
     g = torch.Generator(device="cuda")
-    g.manual_seed(4000)
+    g.manual_seed(S)
     layers, xs, hres = [], [], []
     for i in range(R):
         router = (torch.randn(E, H, generator=g, device="cuda") * synth.ROUTER_STD).to(torch.bfloat16)
@@ -364,7 +400,7 @@ def bench_batch(cfg, args):
         x = (h / torch.sqrt(torch.mean(h * h, dim=1, keepdim=True) + 1e-6)).to(torch.bfloat16)
         layers.append(moe.Layer(hidden=H, inter=I, n_experts=E, top_k=K,
                                 bits_routed=cfg.bits_routed, bits_shared=cfg.bits_shared,
-                                renorm=True, router=router, gate_vec=gate, experts=pool,
+                                renorm=OPTS["renorm"], router=router, gate_vec=gate, experts=pool,
                                 expert_stride=rb, shared_expert=shared[i * sb:(i + 1) * sb]))
         xs.append(x.contiguous())
         hres.append(h.contiguous())
@@ -413,7 +449,7 @@ def bench_gdn(args):
     import torch
     from bit_dequant_expert_route_amd import moe
     g = torch.Generator(device="cuda")
-    g.manual_seed(4500)
+    g.manual_seed(4500 + OPTS["seed"])
     L, Hh, dk, dv = GDN_LAYERS, GDN_HEADS, GDN_DK, GDN_DV
     states = [torch.randn(1, Hh, dv, dk, generator=g, device="cuda") * 0.1 for _ in range(L)]
     def unit(t):
@@ -571,20 +607,21 @@ def bench_tier(cfg, args):
     rb = synth.record_layout(H, I, cfg.bits_routed).total
     sb = synth.record_layout(H, I, cfg.bits_shared).total
     pool = torch.empty(E * rb, dtype=torch.uint8, device="cuda")
-    moe.fill_experts(pool, rb, E, 5000, 0, 0, H, I, cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
+    S = 5000 + OPTS["seed"]
+    moe.fill_experts(pool, rb, E, S, 0, 0, H, I, cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
     host = torch.empty(E * rb, dtype=torch.uint8, pin_memory=True)
     host.copy_(pool)
     torch.cuda.synchronize()
     shared = torch.empty(sb, dtype=torch.uint8, device="cuda")
-    moe.fill_experts(shared, sb, 1, 5000, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared,
+    moe.fill_experts(shared, sb, 1, S, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared,
                      synth.dist_for_bits(cfg.bits_shared))
     cache = torch.empty(S * rb, dtype=torch.uint8, device="cuda")
     g = torch.Generator(device="cuda")
-    g.manual_seed(5000)
+    g.manual_seed(S)
     router = (torch.randn(E, H, generator=g, device="cuda") * synth.ROUTER_STD).to(torch.bfloat16)
     gate = (torch.randn(H, generator=g, device="cuda") * synth.GATEVEC_STD).to(torch.bfloat16)
     layer = moe.Layer(hidden=H, inter=I, n_experts=E, top_k=K, bits_routed=cfg.bits_routed,
-                      bits_shared=cfg.bits_shared, renorm=True, router=router, gate_vec=gate,
+                      bits_shared=cfg.bits_shared, renorm=OPTS["renorm"], router=router, gate_vec=gate,
                       experts=pool, expert_stride=rb, shared_expert=shared)
     tier = moe.Tier(host, E, rb, cache, S)
     hs = torch.empty(W + N, H, device="cuda")
@@ -734,7 +771,7 @@ def main():
         return
 
     read_gbps = read_peak_gbps()
-    cfg = synth.CONFIGS["q4_layer" if args.workload == "q4_tier" else args.workload]
+    cfg = workload_config(args)
     kb = kernel_bytes(cfg)
     if args.workload == "q4_tier":
         ms_tok, rec, extra = bench_tier(cfg, args)
@@ -798,7 +835,7 @@ def main():
                         f"their gated-delta-rule block ({cfg.gdn_heads} heads of {cfg.gdn_head_dim}, 4-bit "
                         f"projections, fp32 state), one token (value = per-token time / {cfg.n_layers})",
         "q4_batch16": f"MoE layer call on {cfg.n_tokens} correlated tokens (value = time per call)",
-    }[cfg.name]
+    }[cfg.name.split("+")[0]]
     line = {
         "metric": METRIC if args.workload != "q4_tier" else
                   "MoE-layer decode latency with the routed experts in host memory (us per token)",

@@ -13,6 +13,7 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -54,10 +55,29 @@ bool prof_active(hipStream_t s) {
   return true;
 }
 
+// MOE_DEBUG=1: every launch outside stream capture is followed by a stream
+// synchronisation, so that a fault or launch error is reported by the call
+// (and the launch) that caused it
+bool debug_sync() {
+  static const bool on = [] {
+    const char *e = getenv("MOE_DEBUG");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+hipError_t debug_check(hipStream_t s, hipError_t e) {
+  if (e != hipSuccess || !debug_sync()) return e;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return e;
+  const hipError_t se = hipStreamSynchronize(s);
+  return se != hipSuccess ? se : hipGetLastError();
+}
+
 // launch `fn` (one kernel) so that its dispatch records a pair of events
 template <class F>
 hipError_t timed(hipStream_t s, int id, F &&fn) {
-  if (!prof_active(s)) return fn();
+  if (!prof_active(s)) return debug_check(s, fn());
   const int i = g_prof.n;
   g_launch_events.start = g_prof.ev[2 * i];
   g_launch_events.stop = g_prof.ev[2 * i + 1];
@@ -66,7 +86,7 @@ hipError_t timed(hipStream_t s, int id, F &&fn) {
   if (e != hipSuccess) return e;
   g_prof.ids[i] = id;
   g_prof.n = i + 1;
-  return hipSuccess;
+  return debug_check(s, hipSuccess);
 }
 
 size_t up256(size_t n) { return (n + 255u) / 256u * 256u; }
@@ -1105,7 +1125,9 @@ int moe_tier_destroy(moe_tier_t t) {
 
 int moe_tier_reset(moe_tier_t t, void *stream) {
   if (!t) return fail(MOE_EINVAL, "tier is NULL");
-  MOE_TRY_HIP(launch_tier_reset(t->state, t->n_slots, static_cast<hipStream_t>(stream)), "tier reset launch");
+  MOE_TRY_HIP(debug_check(static_cast<hipStream_t>(stream),
+                          launch_tier_reset(t->state, t->n_slots, static_cast<hipStream_t>(stream))),
+              "tier reset launch");
   return MOE_OK;
 }
 
@@ -1370,7 +1392,8 @@ int moe_fill_experts(void *dst, size_t stride, int n, uint64_t seed, int layer, 
   p.bias_lo = bias_lo;
   p.bias_hi = bias_hi;
   p.off = off;
-  MOE_TRY_HIP(launch_fill(p, static_cast<hipStream_t>(stream)), "fill launch");
+  MOE_TRY_HIP(debug_check(static_cast<hipStream_t>(stream), launch_fill(p, static_cast<hipStream_t>(stream))),
+              "fill launch");
   return MOE_OK;
 }
 
@@ -1422,7 +1445,8 @@ int moe_profile_end(float *ms, int *kernel_ids, int capacity, int *n_out) {
 int moe_zero(void *ptr, size_t bytes, void *stream) {
   if (!ptr) return fail(MOE_EINVAL, "ptr is NULL");
   if (!aligned(ptr, 16)) return fail(MOE_EALIGN, "ptr must be 16-byte aligned");
-  MOE_TRY_HIP(launch_zero(ptr, bytes, static_cast<hipStream_t>(stream)), "zero launch");
+  MOE_TRY_HIP(debug_check(static_cast<hipStream_t>(stream), launch_zero(ptr, bytes, static_cast<hipStream_t>(stream))),
+              "zero launch");
   return MOE_OK;
 }
 

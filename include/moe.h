@@ -28,6 +28,11 @@
  *     moe_last_error() (thread-local).  A failed kernel launch returns
  *     MOE_EHIP with the HIP error string.  Faults inside kernels surface at the
  *     caller's next stream synchronisation.
+ *   - Environment: MOE_DEBUG=1 makes every call synchronise its stream after
+ *     each launch made outside stream capture and return MOE_EHIP for a
+ *     launch that faulted (triage only: it breaks the no-synchronisation
+ *     rule above).  MOE_TUNE="gu=<p>,dn=<p>,sh=<p>" (p = 1, 2 or 4) overrides
+ *     the rows a wave takes per pass in the gate/up, down and shared kernels.
  *   - Kernels never read outside the buffers described here.  An expert id
  *     that is neither in [0, n_experts) nor MOE_SHARED yields a NaN row.
  *   - Limits: bits 4 or 2, group 64 (else MOE_EUNSUPPORTED); hidden and inter
