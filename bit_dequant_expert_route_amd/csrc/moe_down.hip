@@ -263,17 +263,12 @@ hipError_t launch_partials(const PartialsParams &p, hipStream_t s) {
 
 
 // the combine kernel's shape: rows per wave, whether the SwiGLU outputs go
-// through LDS, and the workgroup form (sixteen or eight waves, or split pairs).
-// Sixteen-wave workgroups (4-bit rows of one code chunk, one pass, a wave per
-// row for every wave slot of 256 CUs) stage the SwiGLU outputs half as often
-// and halve the stack's partial-sum additions (60-layer q4 stack: 21.08
-// against 21.23 us per layer; the single q4 layer unchanged).
-constexpr bool kSixteenWaves = true;
+// through LDS, and the workgroup form (eight waves, or split pairs)
 struct CombineShape {
   int rows_per_wave;
-  bool use_lds, sixteen, eight, split;
+  bool use_lds, eight, split;
   size_t lds;
-  int wg_rows() const { return (sixteen ? 16 : eight ? 8 : (split ? 2 : 4)) * rows_per_wave; }
+  int wg_rows() const { return (eight ? 8 : (split ? 2 : 4)) * rows_per_wave; }
 };
 
 static CombineShape combine_shape(int H, int I, int bits, int n_vectors) {
@@ -291,11 +286,10 @@ static CombineShape combine_shape(int H, int I, int bits, int n_vectors) {
   c.lds = c.use_lds ? hbytes : 0;
   // eight-wave workgroups when there are enough waves for one per CU (q4
   // layer: 20.85 against 21.15 us; with 1024 waves, half the CUs would idle)
-  c.sixteen = kSixteenWaves && bits == 4 && c.use_lds && nch == 1 && npass == 1 && waves >= 16 * kCUs;
-  c.eight = c.use_lds && !c.sixteen && waves >= 8 * kCUs;
+  c.eight = c.use_lds && waves >= 8 * kCUs;
   // otherwise (fewer rows) two waves share each set of rows, splitting the
   // experts, so that the grid still has waves to hide latency with
-  c.split = c.use_lds && !c.sixteen && !c.eight;
+  c.split = c.use_lds && !c.eight;
   return c;
 }
 
@@ -317,10 +311,9 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
     const CombineShape cs = combine_shape(p.H, p.I, bits, p.K + (shared_in ? 1 : 0));
     const int waves = (p.H + p.rows_per_wave - 1) / p.rows_per_wave;
     const bool k4 = p.K <= 4;
-    const bool sixteen = cs.sixteen, eight = cs.eight, split = cs.split;
+    const bool eight = cs.eight, split = cs.split;
     const size_t lds = cs.lds;
-    const dim3 grid(sixteen ? (waves + 15) / 16
-                            : eight ? (waves + 7) / 8 : (split ? (waves + 1) / 2 : (waves + 3) / 4));
+    const dim3 grid(eight ? (waves + 7) / 8 : (split ? (waves + 1) / 2 : (waves + 3) / 4));
     // the routing partials need whole workgroup row tiles of 8..64 rows and
     // the SwiGLU outputs in LDS
     if (p.nr_acc && (!shared_in || !combine_takes_partials(p.H, p.I, bits, p.K + 1)))
@@ -329,15 +322,6 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
     // (the partials epilogue is built for stack layers: shared expert in)
 #define MOE_DC(BITS, MAXK, SIN)                                                                       \
   do {                                                                                                \
-    if constexpr (BITS == 4) {                                                                        \
-      if (sixteen) { /* one code chunk, one pass */                                                   \
-        if (epi) MOE_LAUNCH((k_down_combine<BITS, 1, 1, MAXK, SIN, true, 16, false, SIN>), grid,      \
-                            dim3(1024), lds, s, p);                                                   \
-        else MOE_LAUNCH((k_down_combine<BITS, 1, 1, MAXK, SIN, true, 16, false, false>), grid,        \
-                        dim3(1024), lds, s, p);                                                       \
-        break;                                                                                        \
-      }                                                                                               \
-    }                                                                                                 \
     if constexpr (SIN) {                                                                              \
       if (eight && epi) {                                                                             \
         MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, true, 8, false, true>), \
