@@ -117,9 +117,14 @@ def kernel_bytes(cfg):
 
 
 def source_sha():
+    """Hash of every kernel and library source (the counter summaries in
+    profiles/ name the sources they were taken on)."""
     h = hashlib.sha256()
-    for f in ("moe_kernels.hip", "moe_device.h", "moe_api.cpp", "moe_internal.h", "moe_gdn.hip"):
-        h.update(open(os.path.join(ROOT, "bit_dequant_expert_route_amd", "csrc", f), "rb").read())
+    csrc = os.path.join(ROOT, "bit_dequant_expert_route_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -607,17 +612,17 @@ def bench_tier(cfg, args):
     rb = synth.record_layout(H, I, cfg.bits_routed).total
     sb = synth.record_layout(H, I, cfg.bits_shared).total
     pool = torch.empty(E * rb, dtype=torch.uint8, device="cuda")
-    S = 5000 + OPTS["seed"]
-    moe.fill_experts(pool, rb, E, S, 0, 0, H, I, cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
+    seed = 5000 + OPTS["seed"]
+    moe.fill_experts(pool, rb, E, seed, 0, 0, H, I, cfg.bits_routed, synth.dist_for_bits(cfg.bits_routed))
     host = torch.empty(E * rb, dtype=torch.uint8, pin_memory=True)
     host.copy_(pool)
     torch.cuda.synchronize()
     shared = torch.empty(sb, dtype=torch.uint8, device="cuda")
-    moe.fill_experts(shared, sb, 1, S, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared,
+    moe.fill_experts(shared, sb, 1, seed, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared,
                      synth.dist_for_bits(cfg.bits_shared))
     cache = torch.empty(S * rb, dtype=torch.uint8, device="cuda")
     g = torch.Generator(device="cuda")
-    g.manual_seed(S)
+    g.manual_seed(seed)
     router = (torch.randn(E, H, generator=g, device="cuda") * synth.ROUTER_STD).to(torch.bfloat16)
     gate = (torch.randn(H, generator=g, device="cuda") * synth.GATEVEC_STD).to(torch.bfloat16)
     layer = moe.Layer(hidden=H, inter=I, n_experts=E, top_k=K, bits_routed=cfg.bits_routed,
