@@ -20,8 +20,7 @@
  *   [sardonic] education.sardonicrepulsion.com (sk), "Flash-MoE: how to run a
  *       397-billion-parameter AI model on an ordinary notebook"
  *
- * Readings taken where the pages are silent (each is listed with its reason in
- * the design notes of the repository):
+ * Readings taken where the pages are silent:
  *   - codes are unsigned, little-endian inside 32-bit words: element c of a row
  *     sits in word c*b/32 at bit b*(c mod 32/b); rows are contiguous;
  *   - one (scale, bias) pair per 64 consecutive input columns, stored as a

@@ -1,7 +1,7 @@
 """Seeded test cases: inputs from the generator, gap enforcement and expected
 values from the fp64 oracle (never from the HIP path).
 
-Input recipe per workload (see the design notes):
+Input recipe per workload:
   tiny       x ~ N(0,1) fp32 and h_res ~ N(0,1) fp32, independent
   q4/q2      h_res ~ N(0,1) fp32, x = bf16(RMSNorm(h_res)) (RMSNorm in fp64)
   stacks     h0 ~ N(0,1) fp32; per layer a bf16 N(0,1) update u_l, then

@@ -68,7 +68,10 @@ def _check(case, h, idx_log, w_log, states):
         assert err_metric(w_by, case.w[l]) <= TOL, (l, w_by, case.w[l])
         if case.states[l] is not None:
             # the state of a layer: n_heads * d_head^2 values (a million at
-            # 64 x 128 x 128); checked normwise, see the design notes
+            # 64 x 128 x 128), checked normwise: the recurrence carries each
+            # layer's rounding into the next layers, so single entries near
+            # zero differ in relative terms by more than the floored
+            # elementwise bound while the state as a whole agrees to ~1e-5
             en, ee = normwise(states[l], case.states[l]), err_metric(states[l], case.states[l])
             log(f"  layer {l} state: normwise {en:.2e}, floored elementwise {ee:.2e}")
             assert en <= TOL, (l, en)
