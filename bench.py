@@ -192,34 +192,44 @@ def build_rotation(cfg, R, seed0=1000):
 
 def cpu_baseline(cfg, budget_s):
     """fp64 oracle on the host: route + K routed experts + shared + combine for
-    as many sampled layer instances as fit the time budget, on all the
-    oracle's threads, then on one thread for a third of that budget."""
+    as many layer instances as fit the time budget, on all the oracle's
+    threads, then on one thread for a third of that budget.  The instances
+    are the timed rotation's first ones (same routers, gate vectors, x,
+    residuals and records) when the GPU leg kept them, else fresh draws of
+    the same recipe."""
     import oracle
     from bit_dequant_expert_route_amd import synth
     orc = oracle.get()
     H, I = cfg.hidden, cfg.inter
+    rot = ROTATION_HOST if ROTATION_HOST.get("cfg") == cfg.name else None
+
+    def inputs(i, first):
+        if rot:
+            d = rot["instances"][i % len(rot["instances"])]
+            return (rot["seed0"], d["router"], d["gate"], d["x"], d["h_res"], d["shared_id"])
+        seed = first + i
+        h_res = synth.residual(cfg, seed)
+        x64 = orc.rmsnorm(h_res.astype(np.float64))
+        xb = synth.bf16_to_f32(synth.f64_to_bf16_rne(x64)).astype(np.float64)
+        return (seed, synth.router_weights(cfg, seed), synth.shared_gate_vector(cfg, seed), xb,
+                h_res.astype(np.float64), synth.SHARED_GEN_ID)
 
     def sample(budget, first):
         times = []
         t_end = time.perf_counter() + budget
         i = 0
         while time.perf_counter() < t_end or i == 0:
-            seed = first + i
-            router = synth.router_weights(cfg, seed)
-            gate = synth.shared_gate_vector(cfg, seed)
-            h_res = synth.residual(cfg, seed)
-            x64 = orc.rmsnorm(h_res.astype(np.float64))
-            xb = synth.bf16_to_f32(synth.f64_to_bf16_rne(x64)).astype(np.float64)
+            seed, router, gate, xb, h_res, shared_id = inputs(i, first)
             # weight generation is excluded from the timed region
             logits = orc.router(router, cfg.router_dtype, xb)
             idx = orc.topk(logits, cfg.top_k)
             recs = [synth.make_record(seed, 0, int(e), H, I, cfg.bits_routed) for e in idx]
-            shared = synth.make_record(seed, 0, synth.SHARED_GEN_ID, H, I, cfg.bits_shared)
+            shared = synth.make_record(seed, 0, shared_id, H, I, cfg.bits_shared)
             t0 = time.perf_counter()
-            r = orc.route(router, cfg.router_dtype, gate, cfg.gate_dtype, xb, cfg.top_k, True)
+            r = orc.route(router, cfg.router_dtype, gate, cfg.gate_dtype, xb, cfg.top_k, OPTS["renorm"])
             ys = [orc.expert(rec, H, I, cfg.bits_routed, xb)[1] for rec in recs]
             ysh = orc.expert(shared, H, I, cfg.bits_shared, xb)[1]
-            orc.combine(h_res.astype(np.float64), np.stack(ys), r["w"], ysh, r["sigma"])
+            orc.combine(h_res, np.stack(ys), r["w"], ysh, r["sigma"])
             times.append(time.perf_counter() - t0)
             i += 1
         return times
@@ -231,8 +241,10 @@ def cpu_baseline(cfg, budget_s):
         one = sample(budget_s / 3.0, 6000)
     finally:
         orc.set_threads(threads)
+    which = (f"cycling over the first {len(rot['instances'])} layer instances of the timed rotation"
+             if rot else "fresh draws of the workload's recipe")
     return dict(value=float(np.median(times) * 1e6), unit="us", cores=threads, kind="oracle",
-                sample=f"{len(times)} single-token layer decodes of the {cfg.name} workload "
+                sample=f"{len(times)} single-token layer decodes of the {cfg.name} workload, {which} "
                        f"(fp64 oracle, OpenMP over output rows, weight generation excluded), median",
                 value_1_core=float(np.median(one) * 1e6), sample_1_core=f"{len(one)} more decodes on one thread, median",
                 cpu_model=cpu_model())
@@ -544,7 +556,34 @@ def bench_layer(cfg, args):
     extra = {"replay_us_per_layer_median": round(float(np.median(per)), 3),
              "replay_us_per_layer_p90": round(float(np.percentile(per, 90)), 3)}
     extra.update(launch_inclusive(layers, xs, hres, out, idx, w, ws, args))
+    keep_for_cpu(cfg, layers, xs, hres)
     return ms_layer, rec, extra
+
+
+# host copies of the first rotation instances, for the CPU oracle leg
+ROTATION_HOST = {}
+CPU_INSTANCES = 32
+
+
+def keep_for_cpu(cfg, layers, xs, hres):
+    """Copy the router, gate vector, x and residual of the first instances of
+    the timed rotation to the host (after the timed region), so that the CPU
+    leg decodes the same layers; their records are regenerated on the host,
+    bit-identical to the device fill."""
+    import torch
+    from bit_dequant_expert_route_amd import synth
+
+    def host(t):
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+    insts = []
+    for i in range(min(len(layers), CPU_INSTANCES)):
+        x = host(xs[i])
+        x64 = (synth.bf16_to_f32(x) if x.dtype == np.uint16 else x).astype(np.float64)
+        insts.append(dict(router=host(layers[i].router), gate=host(layers[i].gate_vec), x=x64,
+                          h_res=host(hres[i]).astype(np.float64), shared_id=synth.SHARED_GEN_ID + i))
+    ROTATION_HOST.update(cfg=cfg.name, seed0=1000 + OPTS["seed"], instances=insts)
 
 
 def launch_inclusive(layers, xs, hres, out, idx, w, ws, args):

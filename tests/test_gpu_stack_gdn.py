@@ -140,6 +140,12 @@ GDN_EDGE = {
     "ragged_h128": dataclasses.replace(synth.CONFIGS["tiny_stack_gdn"], name="gdn_ragged_h128",
                                        hidden=192, inter=320, bits_routed=2, bits_shared=2,
                                        gdn_heads=1, gdn_head_dim=128, n_layers=5),
+    # output projections of whole column segments (one 16-byte code chunk per
+    # lane): one segment of 2,048 columns at 4 bits, two of 4,096 at 2 bits
+    "q4_seg1": dataclasses.replace(synth.CONFIGS["tiny_stack_gdn"], name="gdn_q4_seg1",
+                                   gdn_heads=16, gdn_head_dim=128, n_layers=5),
+    "q2_seg2": dataclasses.replace(synth.CONFIGS["tiny_stack_gdn"], name="gdn_q2_seg2",
+                                   gdn_heads=64, gdn_head_dim=128, gdn_bits=2, n_layers=5),
 }
 
 
