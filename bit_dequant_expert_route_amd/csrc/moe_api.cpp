@@ -571,19 +571,32 @@ int layer_batch(const moe_layer_t *L, int T, int xsrc, const void *x, const floa
   hp.xs_sum_stride = (int)wl.xs_sum_stride;
   MOE_TRY_HIP(timed(s, MOE_KERNEL_HEAD, [&] { return launch_head(hp, s); }), "router launch");
 
+  // every token's selection in a workgroup of its own, then the grouping in
+  // one workgroup (a single workgroup selecting for every token took 12.8 us
+  // of the 16-token q4 call)
+  TopkParams tp;
+  tp.logits = logits;
+  tp.T = T;
+  tp.E = L->n_experts;
+  tp.K = L->top_k;
+  tp.renorm = L->renorm_topk;
+  tp.idx = idx;
+  tp.w = w;
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_TOPK, [&] { return launch_topk(tp, s); }), "top-K launch");
   RouteGroupParams rg;
   rg.logits = logits;
   rg.T = T;
   rg.E = L->n_experts;
   rg.K = L->top_k;
   rg.renorm = L->renorm_topk;
+  rg.selected = 1;
   rg.idx = idx;
   rg.w = w;
   rg.g_count = g_count;
   rg.g_expert = g_expert;
   rg.g_start = g_start;
   rg.g_pair = g_pair;
-  MOE_TRY_HIP(timed(s, MOE_KERNEL_TOPK, [&] { return launch_route_group(rg, s); }), "top-K/group launch");
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_TOPK, [&] { return launch_route_group(rg, s); }), "grouping launch");
 
   GroupedParams gp;
   memset(&gp, 0, sizeof gp);

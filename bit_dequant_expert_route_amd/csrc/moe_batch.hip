@@ -25,14 +25,18 @@ __global__ __launch_bounds__(kGroupBlock) void k_route_group(RouteGroupParams p)
   __shared__ int n_first;
   const int wv = threadIdx.x >> 6, lane = lane_id();
   if (threadIdx.x == 0) n_first = 0;
-  for (int t = wv; t < p.T; t += kGroupBlock / 64) {
-    float v[kTopkNpl];
-    topk_load(p.logits + (size_t)t * p.E, p.E, v);
-    int e;
-    float w;
-    topk_select(v, p.E, p.K, p.renorm, e, w);
-    topk_store(e, w, p.K, p.idx + (size_t)t * p.K, p.w + (size_t)t * p.K);
-    if (lane < p.K) pe[t * p.K + lane] = e;
+  if (p.selected) {  // the selection is in p.idx already (k_topk)
+    for (int q = threadIdx.x; q < p.T * p.K; q += kGroupBlock) pe[q] = p.idx[q];
+  } else {
+    for (int t = wv; t < p.T; t += kGroupBlock / 64) {
+      float v[kTopkNpl];
+      topk_load(p.logits + (size_t)t * p.E, p.E, v);
+      int e;
+      float w;
+      topk_select(v, p.E, p.K, p.renorm, e, w);
+      topk_store(e, w, p.K, p.idx + (size_t)t * p.K, p.w + (size_t)t * p.K);
+      if (lane < p.K) pe[t * p.K + lane] = e;
+    }
   }
   __syncthreads();
   const int P = p.T * p.K;

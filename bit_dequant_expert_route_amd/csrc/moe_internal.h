@@ -77,6 +77,7 @@ hipError_t launch_head(const HeadParams &p, hipStream_t s);
 struct RouteGroupParams {
   const float *logits;            // [T][E]
   int T, E, K, renorm;
+  int selected;                   // 1: idx holds the selection; only group
   int32_t *idx;                   // [T][K]
   float *w;                       // [T][K]
   int32_t *g_count;               // [1]  number of distinct experts U

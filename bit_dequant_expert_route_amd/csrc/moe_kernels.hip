@@ -118,14 +118,30 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadParams p) {
 // ---------------------------------------------------------------------------
 // stand-alone top-K (one wave per token)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_topk(TopkParams p) {
+// one workgroup per token, the selection split over its four waves (as in
+// the gate/up kernel: each wave selects over a quarter of the experts, then
+// one wave merges the 4 K candidates)
+__global__ __launch_bounds__(kBlock) void k_topk(TopkParams p) {
+  __shared__ TopkShare tsh;
+  static_assert(kBlock / 64 == 4, "the selection is split over four waves");
   const int t = blockIdx.x;
-  float v[kTopkNpl];
-  topk_load(p.logits + (size_t)t * p.E, p.E, v);
-  int e;
-  float w;
-  topk_select(v, p.E, p.K, p.renorm, e, w);
-  topk_store(e, w, p.K, p.idx + (size_t)t * p.K, p.w + (size_t)t * p.K);
+  const int wv = wave_uniform(threadIdx.x >> 6);
+  const float *lg = p.logits + (size_t)t * p.E;
+  float lv[4];
+  if (topk_npl(p.E) == 2) {
+    topk_part_load<2>(lg, p.E, wv, lv);
+    topk_part_select<2>(lv, p.E, p.K, p.renorm, wv, tsh);
+  } else {
+    topk_part_load<4>(lg, p.E, wv, lv);
+    topk_part_select<4>(lv, p.E, p.K, p.renorm, wv, tsh);
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  int sel_e = -2;
+  uint32_t sel_key = 0, top_key = 0;
+  topk_merge(tsh, p.E, p.K, sel_e, sel_key, top_key);
+  topk_store(sel_e, topk_merge_weight(tsh, p.K, p.renorm, sel_e, sel_key, top_key), p.K,
+             p.idx + (size_t)t * p.K, p.w + (size_t)t * p.K);
 }
 
 // ---------------------------------------------------------------------------
@@ -518,7 +534,7 @@ hipError_t launch_head(const HeadParams &p0, hipStream_t s) {
 }
 
 hipError_t launch_topk(const TopkParams &p, hipStream_t s) {
-  MOE_LAUNCH(k_topk, dim3(p.T), dim3(64), 0, s, p);
+  MOE_LAUNCH(k_topk, dim3(p.T), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
