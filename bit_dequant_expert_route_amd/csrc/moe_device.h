@@ -396,13 +396,6 @@ __device__ __forceinline__ XStage<BITS, false> read_stage(const uint32_t *xs_pai
 //           is the column sum (the XS_LDSPAD layout); thread t stores the
 //           four columns 4t + 4 kBlock i.
 // ---------------------------------------------------------------------------
-// Whether the gate/up kernel stages x in LDS: when a wave's own chunks of x
-// would outweigh its weight rows (fp32 x, or 2-bit codes).  For 4-bit codes
-// and bf16 x (as many bytes of x as of weights per wave) each wave staging its
-// chunks itself was measured faster (q4 layer 21.5 against 21.8 us).
-__host__ __device__ constexpr bool gateup_x_in_lds(int bits, int xs) {
-  return xs != XS_BF16 || bits == 2;
-}
 
 template <int BITS, bool XF32>
 struct XLds {

@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kBlock) void k_down_y(DownParams p) {
   const int row0 = wie * p.rows_per_wave;
   // a null id list selects the shared expert for every slot
   const int id = p.ids ? wave_uniform(p.ids[slot]) : kSharedId;
-  // unreadable entries (see k_gateup) read routed record 0 and yield NaN
+  // unreadable entries (as in k_gateup_xl) read routed record 0 and yield NaN
   const bool shared = id == kSharedId;
   const bool valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
   const bool from_shared = shared && valid;

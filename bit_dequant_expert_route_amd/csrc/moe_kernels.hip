@@ -183,103 +183,11 @@ __device__ __forceinline__ void copy_down_part(const GateUpParams &p, int c) {
     }
   }
 }
-template <int BITS, int NCH, int NPASS, int XS>
-__global__ __launch_bounds__(kBlock) void k_gateup(GateUpParams p) {
-  // each wave stages its own chunks of x (see gateup_x_in_lds)
-  __shared__ TopkShare tsh;
-  static_assert(kBlock / 64 == 4, "the selection is split over four waves");
-  const int blk = wave_uniform(blockIdx.x);
-  const int wv = wave_uniform(threadIdx.x >> 6);
-  // The routed workgroups come first in the grid, so they are dispatched and
-  // issue their logit loads ahead of the shared expert's: those need no
-  // routing and stream the shared rows while the routed ones select experts
-  // (q4 layer 20.36 -> 20.10 us per layer with this order)
-  const int n_routed_blocks = (int)gridDim.x - p.n_shared_blocks - p.n_copy_blocks;
-  if (blk >= n_routed_blocks + p.n_shared_blocks) {  // workgroup-uniform: a tier copy
-    copy_down_part(p, blk - n_routed_blocks - p.n_shared_blocks);
-    return;
-  }
-  const bool shared_blk = blk >= n_routed_blocks;
-  const int wave = shared_blk ? (blk - n_routed_blocks) * (kBlock / 64) + wv
-                              : blk * (kBlock / 64) + wv;
-  const int slot = shared_blk ? 0 : wave / p.waves_per_expert;
-  const int wie = shared_blk ? wave : wave - slot * p.waves_per_expert;
-  const bool topk = !shared_blk && !p.ids;  // workgroup-uniform
-  if (!topk && (shared_blk ? wie >= p.waves_per_expert : slot >= p.n)) return;
-
-  // Routing: the four waves of the workgroup each take a quarter of the
-  // logits, and after one barrier each merges the quarters' candidates.
-  // Loads go out in the order they are needed (vmcnt counts in order):
-  // logits, x, then the weights once the expert is known.
-  float lv[4];
-  const int npl = topk_npl(p.E);
-  if (topk) {
-    if (npl == 2) topk_part_load<2>(p.logits, p.E, wv, lv);
-    else topk_part_load<4>(p.logits, p.E, wv, lv);
-  }
-  constexpr bool XF32 = XS != XS_BF16;
-  const RowMap m = row_map<BITS>(p.H);
-  const int row0 = wie * p.rows_per_wave;
-  XStage<BITS, XF32> xs[NCH];
-  XRaw<BITS, XS> xr[NCH];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = m.li + (j << m.lg);
-    xr[j] = load_raw<BITS, XS>(p.x, nullptr, c < m.cpr ? c : 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  int id;
-  float *hout;
-  int sel_e = -2;
-  uint32_t sel_key = 0, top_key = 0;
-  if (shared_blk) {
-    id = kSharedId;
-    hout = p.h_shared_out;
-  } else {
-    if (topk) {
-      // the selection gates every routed load of the workgroup: issue it
-      // ahead of the shared-expert waves computing on the same SIMD
-      __builtin_amdgcn_s_setprio(3);
-      if (npl == 2) topk_part_select<2>(lv, p.E, p.K, p.renorm, wv, tsh);
-      else topk_part_select<4>(lv, p.E, p.K, p.renorm, wv, tsh);
-      __syncthreads();
-      if (slot >= p.n) return;
-      topk_merge(tsh, p.E, p.K, sel_e, sel_key, top_key);
-      __builtin_amdgcn_s_setprio(0);
-      id = __builtin_amdgcn_readlane(sel_e, slot);
-    } else {
-      id = wave_uniform(p.ids[slot]);
-    }
-    hout = p.h_out + (size_t)slot * p.I;
-  }
-  // an entry whose record cannot be read at this width (an id out of range,
-  // or the shared expert at another width) reads routed record 0 with the
-  // routed geometry, so every load stays inside the records, and yields NaN
-  const bool shared = id == kSharedId;
-  const bool valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
-  const bool from_shared = shared && valid;
-  const uint8_t *rec = from_shared ? p.shared_rec : p.experts + (size_t)(valid && !shared ? id : 0) * p.stride;
-  uint8_t *fill = nullptr;
-  if (p.rec_src && !shared_blk && valid && !shared) {  // the tier's record of this entry
-    rec = reinterpret_cast<const uint8_t *>(wave_uniform_u64(p.rec_src[slot]));
-    fill = reinterpret_cast<uint8_t *>(wave_uniform_u64(p.rec_fill[slot]));
-  }
-  GUTile<BITS, NCH, NPASS> tile;
-  gu_load(tile, rec, from_shared ? p.soff : p.off, m, p.I, row0);
-  __builtin_amdgcn_sched_barrier(0);
-  if (fill) gu_store(tile, fill, p.off, m, p.I, row0);
-  // the first routed workgroup also reports the selection and its weights
-  if (topk && blk == 0 && wv == 0)
-    topk_store(sel_e, topk_merge_weight(tsh, p.K, p.renorm, sel_e, sel_key, top_key), p.K,
-               p.idx_out, p.w_out);
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) xs[j] = stage_raw<BITS, XS>(xr[j]);
-  gu_compute(tile, xs, m, p.I, row0, valid, hout);
-}
-
-// K2 with x staged once per workgroup in LDS (XLds): the same work, for
-// shapes where a wave's own chunks of x would outweigh its weight rows
+// K2 with x staged once per workgroup in LDS (XLds): each thread loads a slice
+// of x before the one barrier, and the waves read their chunks from LDS.
+// (Each wave staging its own chunks of x, once faster for 4-bit rows with
+// bf16 x, lost once the waves took one row each: q4 layer 20.31 against
+// 19.24 us per layer for this kernel at one row per wave.)
 // ACC: a stack layer's launch, routing from the accumulators (p.acc)
 template <int BITS, int NCH, int NPASS, int XS, bool ACC>
 __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
@@ -342,7 +250,10 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
   float *const hout = shared_blk ? p.h_shared_out : p.h_out + (size_t)slot * p.I;
   uint8_t *fill = nullptr;
   auto issue = [&](int id) {
-    // unreadable entries (see k_gateup) read routed record 0 and yield NaN
+    // an entry whose record cannot be read at this width (an id out of
+    // range, or the shared expert at another width) reads routed record 0
+    // with the routed geometry, so every load stays inside the records, and
+    // yields NaN
     const bool shared = id == kSharedId;
     valid = shared ? (p.shared_ok != 0) : (id >= 0 && id < p.E);
     const bool from_shared = shared && valid;
@@ -542,14 +453,12 @@ hipError_t launch_gateup(const GateUpParams &p0, hipStream_t s) {
   GateUpParams p = p0;
   const int nch = nch_for(p.H, p.bits);
   const int rpp = rpp_for(p.H, p.bits);
-  // one pass where each wave stages its own x (4-bit rows, bf16 x: 4,096
-  // routed waves instead of 2,048 shorten the compute after the selection,
-  // q4 layer 20.95 -> 20.48 us per layer); two where x is staged once per
-  // workgroup (fewer workgroups staging it: the stack 22.7 -> 21.2 us) and
-  // for the host-memory tier (rows read over the link in longer runs:
-  // 116.2 -> 113.8 us per token)
-  const bool per_wave_x = !(p.bits == 4 ? gateup_x_in_lds(4, p.xsrc) : gateup_x_in_lds(2, p.xsrc));
-  const bool one_pass = rpp >= 2 || (per_wave_x && !p.rec_src);
+  // one pass with bf16 x (q4 layer: 4,096 routed waves of one gate and one up
+  // row instead of 2,048 of two share the compute after the selection,
+  // 20.49 -> 19.24 us per layer); two with fp32 x (16 KiB of x staged per
+  // workgroup: the stack 21.2 against 22.7 us with one) and for the
+  // host-memory tier (rows read over the link in longer runs)
+  const bool one_pass = rpp >= 2 || (p.xsrc == XS_BF16 && !p.rec_src);
   const int npass = clamp_pass(nch, pick_pass(tune().gu, one_pass ? 1 : 2));
   p.rows_per_wave = npass * rpp;
   p.waves_per_expert = (p.I + p.rows_per_wave - 1) / p.rows_per_wave;
@@ -564,21 +473,16 @@ hipError_t launch_gateup(const GateUpParams &p0, hipStream_t s) {
   const dim3 grid(p.n_shared_blocks + (waves + 3) / 4 + p.n_copy_blocks);
 #define MOE_GU(BITS, XS)                                                                        \
   do {                                                                                           \
-    if constexpr (gateup_x_in_lds(BITS, XS)) {                                                   \
-      const size_t lds = (size_t)(p.H * BITS / 128) * XLds<BITS, XS != XS_BF16>::kWords * 4;    \
-      if constexpr (XS == XS_F32) {                                                              \
-        if (p.acc) {                                                                             \
-          MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_gateup_xl<BITS, NCH_, NP_, XS, true>), grid,    \
-                                              dim3(kBlock), lds, s, p));                         \
-          break;                                                                                 \
-        }                                                                                        \
+    const size_t lds = (size_t)(p.H * BITS / 128) * XLds<BITS, XS != XS_BF16>::kWords * 4;      \
+    if constexpr (XS == XS_F32) {                                                                \
+      if (p.acc) {                                                                               \
+        MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_gateup_xl<BITS, NCH_, NP_, XS, true>), grid,      \
+                                            dim3(kBlock), lds, s, p));                           \
+        break;                                                                                   \
       }                                                                                          \
-      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_gateup_xl<BITS, NCH_, NP_, XS, false>), grid,     \
-                                          dim3(kBlock), lds, s, p));                             \
-    } else {                                                                                     \
-      MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_gateup<BITS, NCH_, NP_, XS>), grid, dim3(kBlock),  \
-                                          0, s, p));                                             \
     }                                                                                            \
+    MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_gateup_xl<BITS, NCH_, NP_, XS, false>), grid,       \
+                                        dim3(kBlock), lds, s, p));                               \
   } while (0)
   // the accumulators (stacks) come with fp32 x
   if (p.acc && p.xsrc != XS_F32) return hipErrorInvalidValue;
