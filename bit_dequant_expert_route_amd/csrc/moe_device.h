@@ -389,9 +389,10 @@ __device__ __forceinline__ XStage<BITS, false> read_stage(const uint32_t *xs_pai
 // once per wave, and the bf16 staging math runs once per chunk.
 //   bf16 x: chunk c holds its staged pairs, the constant part and the column
 //           sum (kPairs + 2 words, rounded up to a multiple of 4 so that each
-//           chunk starts 16-byte aligned); thread kBlock - 1 - c stages it, so
-//           that wave 0 (which selects the experts) stages none while the
-//           chunks fit in the other waves.
+//           chunk starts 16-byte aligned); thread kBlock - 1 - c stages it
+//           (2-bit: threads kBlock - 1 - 2c and kBlock - 2 - 2c, a half
+//           each), so that wave 0 (which selects the experts) stages none
+//           while the chunks fit in the other waves.
 //   fp32 x: chunk c holds its columns, then kLdsPad floats of which the first
 //           is the column sum (the XS_LDSPAD layout); thread t stores the
 //           four columns 4t + 4 kBlock i.
@@ -411,6 +412,13 @@ template <int BITS>
 struct XPart<BITS, XS_BF16> {
   XRaw<BITS, XS_BF16> r;
 };
+// 2-bit rows: a chunk's 64 bf16 columns are split over two threads (an
+// aligned pair of lanes, 32 columns each), so a thread holds 16 registers of
+// x through the selection instead of 32
+template <>
+struct XPart<2, XS_BF16> {
+  uint4 u[4];
+};
 template <int BITS>
 struct XPart<BITS, XS_F32> {
   float4 v[XLds<BITS, true>::kF4];
@@ -419,7 +427,15 @@ struct XPart<BITS, XS_F32> {
 template <int BITS, int XS>
 __device__ __forceinline__ void xpart_load(XPart<BITS, XS> &xp, const void *x, int H) {
   const int t = threadIdx.x;
-  if constexpr (XS == XS_BF16) {
+  if constexpr (BITS == 2 && XS == XS_BF16) {
+    // thread kBlock - 1 - (2 c + h) loads half h of chunk c
+    const int cpr = H / ChunkGeom<2>::kCols;
+    const int q = kBlock - 1 - t, c = q >> 1, h = q & 1;
+    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) +
+                                                       (c < cpr ? c : 0) * ChunkGeom<2>::kCols + 32 * h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xp.u[i] = src[i];
+  } else if constexpr (XS == XS_BF16) {
     const int cpr = H / ChunkGeom<BITS>::kCols;
     const int c = kBlock - 1 - t;
     xp.r = load_raw<BITS, XS_BF16>(x, nullptr, c < cpr ? c : 0);
@@ -437,7 +453,48 @@ template <int BITS, int XS>
 __device__ __forceinline__ void xpart_store(const XPart<BITS, XS> &xp, uint32_t *xw, int H,
                                             float scale = 1.0f) {
   const int t = threadIdx.x;
-  if constexpr (XS == XS_BF16) {
+  if constexpr (BITS == 2 && XS == XS_BF16) {
+    // Half h of a chunk is words 2h and 2h + 1 (columns 32h..32h + 31): its
+    // 16 staged pairs (pair 8w + f = (x[16w + f], x[16w + 8 + f]), times 1/4
+    // for odd f, as stage_chunk forms them) and its partial constant part and
+    // column sum; the two halves' partials are added across the lane pair
+    // (the same sum in both lanes: fp32 addition commutes).
+    constexpr int NP = ChunkGeom<2>::kPairs;
+    static_assert(2 * (kMaxDim / ChunkGeom<2>::kCols) <= kBlock, "two threads per 2-bit chunk");
+    const int q = kBlock - 1 - t, c = q >> 1, h = q & 1;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = xp.u[i];
+      v[8 * i + 0] = bf_lo(u.x); v[8 * i + 1] = bf_hi(u.x);
+      v[8 * i + 2] = bf_lo(u.y); v[8 * i + 3] = bf_hi(u.y);
+      v[8 * i + 4] = bf_lo(u.z); v[8 * i + 5] = bf_hi(u.z);
+      v[8 * i + 6] = bf_lo(u.w); v[8 * i + 7] = bf_hi(u.w);
+    }
+    uint32_t pr[16];
+    float off = 0.f, xs = 0.f;
+#pragma unroll
+    for (int c2 = 0; c2 < 32; ++c2) xs += v[c2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+#pragma unroll
+      for (int f = 0; f < 8; ++f) {
+        const float sc = (f & 1) ? 0.25f : 1.0f;
+        const uint32_t hp = bf16_rne(v[16 * w + f] * sc) | (bf16_rne(v[16 * w + 8 + f] * sc) << 16);
+        pr[8 * w + f] = hp;
+        off = dot2bf(kMagic16, hp, off);
+      }
+    }
+    off += dpp<0xB1>(off);  // quad_perm [1,0,3,2]: the other half's partial
+    xs += dpp<0xB1>(xs);
+    if (c < H / ChunkGeom<2>::kCols) {
+      uint32_t *d = xw + c * XLds<2, false>::kWords;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4 *>(d + 16 * h + 4 * i) = make_uint4(pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]);
+      if (h == 0) *reinterpret_cast<float2 *>(d + NP) = make_float2(off, xs);
+    }
+  } else if constexpr (XS == XS_BF16) {
     constexpr int NP = ChunkGeom<BITS>::kPairs;
     const int c = kBlock - 1 - t;
     if (c < H / ChunkGeom<BITS>::kCols) {
