@@ -744,7 +744,11 @@ def bench_tier(cfg, args):
              # after: the hits' and the shared expert's work overlaps them)
              "transfer_us_per_token": round(t_link, 3),
              "outside_transfer_us_per_token": round(us_tok - t_link, 3),
-             "link_busy_fraction": round(t_link / us_tok, 3)}
+             "link_busy_fraction": round(t_link / us_tok, 3),
+             # transfer time that runs under compute: the resident token's
+             # time plus the transfer, less the measured token time
+             "hidden_transfer_us_per_token": round(us_res + t_link - us_tok, 3),
+             "hidden_transfer_fraction": round((us_res + t_link - us_tok) / t_link, 3) if t_link > 0 else None}
     return us_tok / 1000.0, rec, extra
 
 
