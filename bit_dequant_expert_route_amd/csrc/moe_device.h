@@ -456,35 +456,40 @@ __device__ __forceinline__ void xpart_store(const XPart<BITS, XS> &xp, uint32_t 
   if constexpr (BITS == 2 && XS == XS_BF16) {
     // Half h of a chunk is words 2h and 2h + 1 (columns 32h..32h + 31): its
     // 16 staged pairs (pair 8w + f = (x[16w + f], x[16w + 8 + f]), times 1/4
-    // for odd f, as stage_chunk forms them) and its partial constant part and
-    // column sum; the two halves' partials are added across the lane pair
-    // (the same sum in both lanes: fp32 addition commutes).
+    // for odd f, the pairs stage_chunk forms) and its partial constant part
+    // and column sum; the two halves' partials are added across the lane
+    // pair (the same sum in both lanes: fp32 addition commutes).
     constexpr int NP = ChunkGeom<2>::kPairs;
     static_assert(2 * (kMaxDim / ChunkGeom<2>::kCols) <= kBlock, "two threads per 2-bit chunk");
     const int q = kBlock - 1 - t, c = q >> 1, h = q & 1;
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 u = xp.u[i];
-      v[8 * i + 0] = bf_lo(u.x); v[8 * i + 1] = bf_hi(u.x);
-      v[8 * i + 2] = bf_lo(u.y); v[8 * i + 3] = bf_hi(u.y);
-      v[8 * i + 4] = bf_lo(u.z); v[8 * i + 5] = bf_hi(u.z);
-      v[8 * i + 6] = bf_lo(u.w); v[8 * i + 7] = bf_hi(u.w);
-    }
+    // Loaded word i of the half holds columns 2i (low) and 2i + 1 (high) of
+    // it; pair 8w + f takes columns 16w + f and 16w + 8 + f, i.e. half f % 2
+    // of words 8w + f / 2 and 8w + 4 + f / 2.  Even f: the two low halves as
+    // they are (a byte permute).  Odd f: the two high halves times 1/4 (exact
+    // in fp32 for |x| >= 2^-124), whose upper 16 bits are then the bf16
+    // values (RNE of an exact value keeps them), gathered by a byte permute.
+    const uint32_t *r = reinterpret_cast<const uint32_t *>(xp.u);
     uint32_t pr[16];
-    float off = 0.f, xs = 0.f;
-#pragma unroll
-    for (int c2 = 0; c2 < 32; ++c2) xs += v[c2];
+    float off_e = 0.f, off_o = 0.f;
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
 #pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const float sc = (f & 1) ? 0.25f : 1.0f;
-        const uint32_t hp = bf16_rne(v[16 * w + f] * sc) | (bf16_rne(v[16 * w + 8 + f] * sc) << 16);
-        pr[8 * w + f] = hp;
-        off = dot2bf(kMagic16, hp, off);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t a = r[8 * w + j], b = r[8 * w + 4 + j];
+        const uint32_t ev = __builtin_amdgcn_perm(b, a, 0x05040100u);
+        const uint32_t qa = __float_as_uint(bf_hi(a) * 0.25f), qb = __float_as_uint(bf_hi(b) * 0.25f);
+        const uint32_t od = __builtin_amdgcn_perm(qb, qa, 0x07060302u);
+        pr[8 * w + 2 * j] = ev;
+        pr[8 * w + 2 * j + 1] = od;
+        off_e = dot2bf(kMagic16, ev, off_e);
+        off_o = dot2bf(kMagic16, od, off_o);
       }
     }
+    // the constant part is 16 x over the even pairs and 4 x over the odd
+    // ones, so the column sum is (off_e + 4 off_o) / 16 (scalings by powers
+    // of two)
+    float off = off_e + off_o;
+    float xs = (off_e + 4.0f * off_o) * 0.0625f;
     off += dpp<0xB1>(off);  // quad_perm [1,0,3,2]: the other half's partial
     xs += dpp<0xB1>(xs);
     if (c < H / ChunkGeom<2>::kCols) {
