@@ -10,6 +10,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe_impl {
 
 // ---------------------------------------------------------------------------
@@ -881,7 +883,7 @@ __device__ __forceinline__ void topk_select(float (&v)[kTopkNpl], int E, int K, 
 // candidates itself.  The words carry the expert, so the merge orders equal
 // logits by the lower expert as the one-wave selection does.
 // ---------------------------------------------------------------------------
-struct TopkShare {
+struct alignas(16) TopkShare {
   uint64_t cand[4][kMaxK];
   float pmax[4], psum[4];
 };
@@ -996,6 +998,47 @@ __device__ __forceinline__ void topk_merge(const TopkShare &sh, int E, int K, in
   e_out = my_e;
   key_out = my_k;
   top_key = k0;
+}
+
+// Entry k (wave-uniform, 0 <= k < K) of the same selection alone, for a wave
+// that needs one expert: lane j < 4K counts the candidate words larger than
+// its own (LDS broadcast reads), and the word with exactly k larger ones is
+// the k-th largest.  Real candidates are distinct words; an absent one is 0,
+// and zeros rank after every real word, so a rank that only zeros (or no
+// word) hold gives -2, as in topk_merge.
+__device__ __forceinline__ int topk_merge_one(const TopkShare &sh, int E, int K, int k) {
+  const int lane = lane_id();
+  const bool has = lane < 4 * K;
+  const int j = has ? lane : 0;
+  const int q = j / K;
+  const uint64_t cw = sh.cand[q][j - q * K];
+  // every word is read before any comparison (16-byte broadcast reads, all
+  // in flight together); a word at r >= K is not a candidate and is masked
+  int rank = 0;
+  auto count = [&](auto nr) {
+    constexpr int NR = decltype(nr)::value;
+    uint64_t o[4][NR];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int r = 0; r < NR; r += 2) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(&sh.cand[w][r]);
+        o[w][r] = ((uint64_t)u.y << 32) | u.x;
+        o[w][r + 1] = ((uint64_t)u.w << 32) | u.z;
+      }
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) rank += (r < K && o[w][r] > cw) ? 1 : 0;
+  };
+  if (K <= 4) count(std::integral_constant<int, 4>{});
+  else count(std::integral_constant<int, kMaxK>{});
+  const uint64_t b = __ballot(has && rank == k);
+  if (!b) return -2;
+  const int src = __builtin_ctzll(b);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(cw >> 32), src);
+  const uint32_t ex = 0xFFFFFFFFu - __builtin_amdgcn_readlane((uint32_t)cw, src);
+  return (hi != 0 && ex < (uint32_t)E) ? (int)ex : -2;
 }
 
 // The softmax weight of lane k's selection (lanes k < K; NaN elsewhere):

@@ -276,18 +276,21 @@ __global__ __launch_bounds__(kBlock) void k_gateup_xl(GateUpParams p) {
   xpart_store(xp, xw, p.H, rn);  // x = r v in stacks
   __syncthreads();
   if (!active) return;
-  int sel_e = -2;
-  uint32_t sel_key = 0, top_key = 0;
   if (topk) {
-    topk_merge(tsh, p.E, p.K, sel_e, sel_key, top_key);
+    // each wave needs only its own slot's expert (rank count, no K rounds)
+    const int e = wave_uniform(topk_merge_one(tsh, p.E, p.K, slot));
     __builtin_amdgcn_s_setprio(0);
-    issue(__builtin_amdgcn_readlane(sel_e, slot));
+    issue(e);
   }
   __builtin_amdgcn_sched_barrier(0);
   // the first routed workgroup also reports the selection and its weights
-  if (topk && blk == 0 && wv == 0)
+  if (topk && blk == 0 && wv == 0) {
+    int sel_e = -2;
+    uint32_t sel_key = 0, top_key = 0;
+    topk_merge(tsh, p.E, p.K, sel_e, sel_key, top_key);
     topk_store(sel_e, topk_merge_weight(tsh, p.K, p.renorm, sel_e, sel_key, top_key), p.K,
                p.idx_out, p.w_out);
+  }
   if (fill) gu_store(tile, fill, p.off, m, p.I, row0);
   XStage<BITS, XF32> xs[NCH];
 #pragma unroll

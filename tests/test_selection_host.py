@@ -10,7 +10,8 @@
    lane l sorts the words of experts 8l..8l+7, then K rounds take the wave
    maximum of the lanes' first keys, the lowest lane holding it, and shift
    that lane's list; and the four-wave split (each quarter selects its K,
-   the 4K candidate words are merged by their 64-bit value) -- against a
+   the 4K candidate words are merged by their 64-bit value, or entry by
+   entry by counting the larger words) -- against a
    brute-force stable sort by (logit descending, expert ascending), on
    logits drawn from a small set of values so that ties are frequent."""
 import os
@@ -128,6 +129,32 @@ def select_split(logits, K, npl):
     return [0xFFFFFFFF - (c & 0xFFFFFFFF) for c in cands[:K]]
 
 
+def split_candidates(logits, K, npl):
+    """The 4 K candidate words the four waves leave in LDS: each wave's top K
+    words in descending order, a wave with fewer than K experts padding its
+    list with 0 words."""
+    E = len(logits)
+    R = 64 * npl
+    cands = []
+    for w in range(4):
+        ws = sorted((word(logits[e], e) for e in range(w * R, min((w + 1) * R, E))), reverse=True)[:K]
+        cands += ws + [0] * (K - len(ws))
+    return cands
+
+
+def merge_one(cands, k, E):
+    """Entry k of the merge by rank count (topk_merge_one): lane j's word is
+    entry k if exactly k of the words are larger; the lowest such lane is
+    read; a 0 word, an expert out of range or no such lane gives -2."""
+    ranks = [sum(1 for o in cands if o > c) for c in cands]
+    lanes = [j for j, r in enumerate(ranks) if r == k]
+    if not lanes:
+        return -2
+    c = cands[lanes[0]]
+    ex = 0xFFFFFFFF - (c & 0xFFFFFFFF)
+    return ex if (c >> 32) != 0 and ex < E else -2
+
+
 def brute(logits, K):
     order = sorted(range(len(logits)), key=lambda e: (-float(np.float32(logits[e]) + 0.0)
                                                       if not np.isnan(logits[e]) else np.inf, e))
@@ -146,3 +173,5 @@ def test_selection_with_ties(E, K):
         want = brute(logits, K)
         assert select_lane_lists(net, logits, K) == want
         assert select_split(logits, K, 2 if E <= 512 else 4) == want
+        cands = split_candidates(logits, K, 2 if E <= 512 else 4)
+        assert [merge_one(cands, k, E) for k in range(K)] == want
