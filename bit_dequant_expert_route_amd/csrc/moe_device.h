@@ -1514,18 +1514,37 @@ __device__ __forceinline__ void down_accumulate_staged(const XStage<BITS, true> 
   }
 }
 
+// The same sums with the input staged one code chunk at a time (each pass's
+// partial still takes the chunks in ascending order, so the result is bit for
+// bit that of down_accumulate_staged): one chunk's columns are live at once
+// instead of NCH of them, which keeps rows of several chunks per lane (long
+// input dimensions) within the registers of four waves per SIMD.
 template <int BITS, int NCH, int NPASS, int XS>
 __device__ __forceinline__ void down_accumulate(const float *hin, const RowMap &m, int H,
                                                 int row0, bool valid, float wgt,
                                                 const DnTile<BITS, NCH, NPASS> &t,
                                                 float (&acc)[NPASS]) {
-  XStage<BITS, true> xs[NCH];
+  float part[NPASS];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) part[p] = 0.f;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = m.li + (j << m.lg);
-    xs[j] = make_stage<BITS, XS>(hin, hin, c < m.cpr ? c : 0);
+    const XStage<BITS, true> xs = make_stage<BITS, XS>(hin, hin, c < m.cpr ? c : 0);
+#pragma unroll
+    for (int p = 0; p < NPASS; p += 2) {
+      constexpr int kLast = NPASS - 1;
+      const int p1 = p + 1 <= kLast ? p + 1 : p;
+      const uint32_t s0 = in_tile(m, H, row0, p, j) ? t.sb[p][j] : 0u;
+      const uint32_t s1 = in_tile(m, H, row0, p1, j) ? t.sb[p1][j] : 0u;
+      float d0, d1;
+      chunk_dot2<BITS>(t.q[p][j], t.q[p1][j], xs, 0u, d0, d1);
+      part[p] = fmaf(bf_lo(s0), d0, fmaf(bf_hi(s0), xs.xs, part[p]));
+      if (p1 != p) part[p1] = fmaf(bf_lo(s1), d1, fmaf(bf_hi(s1), xs.xs, part[p1]));
+    }
   }
-  down_accumulate_staged<BITS, NCH, NPASS>(xs, m, H, row0, valid, wgt, t, acc);
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) acc[p] = valid ? fmaf(wgt, part[p], acc[p]) : __builtin_nanf("");
 }
 
 // ---------------------------------------------------------------------------

@@ -24,7 +24,7 @@ namespace moe_impl {
 // forms the next stack layer's routing inputs (p.nr_acc set).
 template <int BITS, int NCH, int NPASS, int MAXK, bool SHARED_IN, bool USE_LDS, int WAVES, bool SPLIT,
           bool EPI>
-__global__ __launch_bounds__(64 * WAVES) void k_down_combine(DownParams p) {
+__global__ __launch_bounds__(64 * WAVES, (MAXK == 1 && BITS == 4) ? 4 : 1) void k_down_combine(DownParams p) {
   constexpr int kThreads = 64 * WAVES;
   static_assert(!SPLIT || WAVES % 2 == 0, "waves pair up");
   // [K (+1)][I]: the SwiGLU outputs, staged once, each code chunk's columns
@@ -351,12 +351,16 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
       MOE_DISPATCH(nch, npass, MOE_LAUNCH((k_down_combine<BITS, NCH_, NP_, MAXK, SIN, false, 4, false, false>), \
                                           grid, dim3(kBlock), 0, s, p));                              \
   } while (0)
+    // one expert and no shared one (the linear-attention block's output
+    // projection): tiles for one expert only, so the kernel keeps few
+    // registers and its waves fit the CUs in one round
+    const bool k1 = p.K == 1 && !shared_in;
     if (bits == 4) {
       if (shared_in) { if (k4) MOE_DC(4, 4, true); else MOE_DC(4, 8, true); }
-      else { if (k4) MOE_DC(4, 4, false); else MOE_DC(4, 8, false); }
+      else { if (k1) MOE_DC(4, 1, false); else if (k4) MOE_DC(4, 4, false); else MOE_DC(4, 8, false); }
     } else {
       if (shared_in) { if (k4) MOE_DC(2, 4, true); else MOE_DC(2, 8, true); }
-      else { if (k4) MOE_DC(2, 4, false); else MOE_DC(2, 8, false); }
+      else { if (k1) MOE_DC(2, 1, false); else if (k4) MOE_DC(2, 4, false); else MOE_DC(2, 8, false); }
     }
 #undef MOE_DC
   } else {
