@@ -217,10 +217,13 @@ __device__ __forceinline__ void chunk_dot2(const uint4 &qa, const uint4 &qb,
   db = b;
 }
 
-template <int BITS>
-__device__ __forceinline__ void chunk_dot2(const uint4 &qa, const uint4 &qb,
-                                           const XStage<BITS, true> &s, uint32_t,
-                                           float &da, float &db) {
+// fp32 input: the byte converts and fp32 FMAs, for two chunks (TWO) or for
+// qa alone (the odd last row of a wave's passes: the masked words pass
+// through an asm barrier, so a second chain over the same chunk would not be
+// merged with the first and would cost its instructions again)
+template <int BITS, bool TWO>
+__device__ __forceinline__ void chunk_dot_f32(const uint4 &qa, const uint4 &qb,
+                                              const XStage<BITS, true> &s, float &da, float &db) {
   float a = 0.f, b = 0.f;
   const uint32_t wa[4] = {qa.x, qa.y, qa.z, qa.w};
   const uint32_t wb[4] = {qb.x, qb.y, qb.z, qb.w};
@@ -229,28 +232,36 @@ __device__ __forceinline__ void chunk_dot2(const uint4 &qa, const uint4 &qb,
     if constexpr (BITS == 4) {
       // bytes of lo: nibbles 0,2,4,6; bytes of hi: nibbles 1,3,5,7
       const uint32_t la = opaque(wa[t] & 0x0F0F0F0Fu), ha = opaque((wa[t] >> 4) & 0x0F0F0F0Fu);
-      const uint32_t lb = opaque(wb[t] & 0x0F0F0F0Fu), hb = opaque((wb[t] >> 4) & 0x0F0F0F0Fu);
+      uint32_t lb = 0, hb = 0;
+      if constexpr (TWO) {
+        lb = opaque(wb[t] & 0x0F0F0F0Fu);
+        hb = opaque((wb[t] >> 4) & 0x0F0F0F0Fu);
+      }
       const float *x = s.v + 8 * t;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t sh = 8 * k;
         const float xl = x[2 * k], xh = x[2 * k + 1];
         const uint32_t qla = k == 3 ? (la >> 24) : ((la >> sh) & 0xFFu);
-        const uint32_t qlb = k == 3 ? (lb >> 24) : ((lb >> sh) & 0xFFu);
         const uint32_t qha = k == 3 ? (ha >> 24) : ((ha >> sh) & 0xFFu);
-        const uint32_t qhb = k == 3 ? (hb >> 24) : ((hb >> sh) & 0xFFu);
         a = fmaf((float)qla, xl, a);
-        b = fmaf((float)qlb, xl, b);
+        if constexpr (TWO) {
+          const uint32_t qlb = k == 3 ? (lb >> 24) : ((lb >> sh) & 0xFFu);
+          b = fmaf((float)qlb, xl, b);
+        }
         a = fmaf((float)qha, xh, a);
-        b = fmaf((float)qhb, xh, b);
+        if constexpr (TWO) {
+          const uint32_t qhb = k == 3 ? (hb >> 24) : ((hb >> sh) & 0xFFu);
+          b = fmaf((float)qhb, xh, b);
+        }
       }
     } else {
       // byte bb of f_k is field 4*bb + k
-      uint32_t fa[4], fb[4];
+      uint32_t fa[4], fb[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         fa[k] = opaque((wa[t] >> (2 * k)) & 0x03030303u);
-        fb[k] = opaque((wb[t] >> (2 * k)) & 0x03030303u);
+        if constexpr (TWO) fb[k] = opaque((wb[t] >> (2 * k)) & 0x03030303u);
       }
       const float *x = s.v + 16 * t;
 #pragma unroll
@@ -258,15 +269,24 @@ __device__ __forceinline__ void chunk_dot2(const uint4 &qa, const uint4 &qb,
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const uint32_t qa8 = bb == 3 ? (fa[k] >> 24) : ((fa[k] >> (8 * bb)) & 0xFFu);
-          const uint32_t qb8 = bb == 3 ? (fb[k] >> 24) : ((fb[k] >> (8 * bb)) & 0xFFu);
           a = fmaf((float)qa8, x[4 * bb + k], a);
-          b = fmaf((float)qb8, x[4 * bb + k], b);
+          if constexpr (TWO) {
+            const uint32_t qb8 = bb == 3 ? (fb[k] >> 24) : ((fb[k] >> (8 * bb)) & 0xFFu);
+            b = fmaf((float)qb8, x[4 * bb + k], b);
+          }
         }
       }
     }
   }
   da = a;
   db = b;
+}
+
+template <int BITS>
+__device__ __forceinline__ void chunk_dot2(const uint4 &qa, const uint4 &qb,
+                                           const XStage<BITS, true> &s, uint32_t,
+                                           float &da, float &db) {
+  chunk_dot_f32<BITS, true>(qa, qb, s, da, db);
 }
 
 // raw x of one chunk as loaded (bf16 words or fp32), before the staging math;
@@ -1505,7 +1525,8 @@ __device__ __forceinline__ void down_accumulate_staged(const XStage<BITS, true> 
       const uint32_t s0 = in_tile(m, H, row0, p, j) ? t.sb[p][j] : 0u;
       const uint32_t s1 = in_tile(m, H, row0, p1, j) ? t.sb[p1][j] : 0u;
       float d0, d1;
-      chunk_dot2<BITS>(t.q[p][j], t.q[p1][j], xs[j], 0u, d0, d1);
+      if (p1 != p) chunk_dot_f32<BITS, true>(t.q[p][j], t.q[p1][j], xs[j], d0, d1);
+      else chunk_dot_f32<BITS, false>(t.q[p][j], t.q[p][j], xs[j], d0, d1);
       part0 = fmaf(bf_lo(s0), d0, fmaf(bf_hi(s0), xs[j].xs, part0));
       part1 = fmaf(bf_lo(s1), d1, fmaf(bf_hi(s1), xs[j].xs, part1));
     }
@@ -1538,7 +1559,8 @@ __device__ __forceinline__ void down_accumulate(const float *hin, const RowMap &
       const uint32_t s0 = in_tile(m, H, row0, p, j) ? t.sb[p][j] : 0u;
       const uint32_t s1 = in_tile(m, H, row0, p1, j) ? t.sb[p1][j] : 0u;
       float d0, d1;
-      chunk_dot2<BITS>(t.q[p][j], t.q[p1][j], xs, 0u, d0, d1);
+      if (p1 != p) chunk_dot_f32<BITS, true>(t.q[p][j], t.q[p1][j], xs, d0, d1);
+      else chunk_dot_f32<BITS, false>(t.q[p][j], t.q[p][j], xs, d0, d1);
       part[p] = fmaf(bf_lo(s0), d0, fmaf(bf_hi(s0), xs.xs, part[p]));
       if (p1 != p) part[p1] = fmaf(bf_lo(s1), d1, fmaf(bf_hi(s1), xs.xs, part[p1]));
     }
