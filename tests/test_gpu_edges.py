@@ -1,7 +1,7 @@
 """Edge cases of the layer path against the oracle: the smallest and largest
 top-K (K = 1, K = E = 8), the largest expert count (E = 1024: the selection's
 second register width), rows that do not fill a wave's lanes (H, I multiples
-of 64 but not of 128), the widest rows (H = 8192: four chunks per lane, also
+of 64 but not of 128, also for 2-bit bf16 x staged by lane pairs), the widest rows (H = 8192: four chunks per lane, also
 with fp32 x staged in LDS), fp32 activations with bf16 weights, the 64-token
 maximum, and run-to-run determinism."""
 import dataclasses
@@ -27,6 +27,9 @@ EDGE = {
     "e600_k8": C("edge_e600k8", 128, 64, 600, 8, 2, 2, "f32", "f32", "f32"),
     "ragged4": C("edge_ragged4", 192, 320, 16, 2, 4, 4, "bf16", "bf16", "bf16"),
     "ragged2": C("edge_ragged2", 192, 320, 16, 2, 2, 2, "f32", "bf16", "f32"),
+    # 2-bit rows of bf16 x with an odd count of 64-column chunks (3): the
+    # lane pairs that stage the chunks' halves end inside a wave
+    "ragged2b": C("edge_ragged2b", 192, 320, 16, 2, 2, 2, "bf16", "bf16", "bf16"),
     "wide4": C("edge_wide4", 8192, 64, 16, 2, 4, 4, "bf16", "bf16", "bf16"),
     "wide2": C("edge_wide2", 8192, 128, 16, 2, 2, 2, "bf16", "bf16", "bf16"),
     # fp32 x at the widest rows: x staged per workgroup fills the most LDS
