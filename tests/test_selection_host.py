@@ -161,7 +161,7 @@ def brute(logits, K):
     return order[:K]
 
 
-@pytest.mark.parametrize("E,K", [(512, 4), (16, 2), (8, 8), (300, 8), (64, 1)])
+@pytest.mark.parametrize("E,K", [(512, 4), (16, 2), (8, 8), (300, 8), (64, 1), (256, 4), (1024, 8), (600, 8)])
 def test_selection_with_ties(E, K):
     net = network()
     rng = np.random.default_rng(E * 10 + K)
@@ -171,7 +171,8 @@ def test_selection_with_ties(E, K):
         if trial % 3 == 0:
             logits = rng.standard_normal(E).astype(np.float32)
         want = brute(logits, K)
-        assert select_lane_lists(net, logits, K) == want
+        if E <= 512:  # the one-wave selection's eight-per-lane layout
+            assert select_lane_lists(net, logits, K) == want
         assert select_split(logits, K, 2 if E <= 512 else 4) == want
         cands = split_candidates(logits, K, 2 if E <= 512 else 4)
         assert [merge_one(cands, k, E) for k in range(K)] == want
