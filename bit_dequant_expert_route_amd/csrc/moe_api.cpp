@@ -596,7 +596,10 @@ int layer_batch(const moe_layer_t *L, int T, int xsrc, const void *x, const floa
   rg.g_expert = g_expert;
   rg.g_start = g_start;
   rg.g_pair = g_pair;
-  MOE_TRY_HIP(timed(s, MOE_KERNEL_TOPK, [&] { return launch_route_group(rg, s); }), "grouping launch");
+  // small batches: the grouped gate/up kernel groups the pairs itself
+  const bool group_in_kernel = T * L->top_k <= kGroupInKernel;
+  if (!group_in_kernel)
+    MOE_TRY_HIP(timed(s, MOE_KERNEL_TOPK, [&] { return launch_route_group(rg, s); }), "grouping launch");
 
   GroupedParams gp;
   memset(&gp, 0, sizeof gp);
@@ -630,13 +633,15 @@ int layer_batch(const moe_layer_t *L, int T, int xsrc, const void *x, const floa
   gr.bits = L->bits_routed;
   gr.do_routed = 1;
   gr.do_shared = same;
+  GroupedParams gr_gu = gr;  // the gate/up launch, which may group the pairs
+  if (group_in_kernel) gr_gu.group_idx = idx;
   GroupedParams gs = gp;  // the shared expert alone, at its own width
   gs.bits = L->bits_shared;
   gs.do_routed = 0;
   gs.do_shared = 1;
   gs.xs_pairs = nullptr;  // x was staged for the routed width
   gs.xs_sums = nullptr;
-  MOE_TRY_HIP(timed(s, MOE_KERNEL_GATEUP, [&] { return launch_gateup_grouped(gr, s); }), "grouped gate/up launch");
+  MOE_TRY_HIP(timed(s, MOE_KERNEL_GATEUP, [&] { return launch_gateup_grouped(gr_gu, s); }), "grouped gate/up launch");
   if (!same)
     MOE_TRY_HIP(timed(s, MOE_KERNEL_GATEUP, [&] { return launch_gateup_grouped(gs, s); }), "shared gate/up launch");
   MOE_TRY_HIP(timed(s, MOE_KERNEL_DOWN_Y, [&] { return launch_down_grouped(gr, s); }), "grouped down launch");

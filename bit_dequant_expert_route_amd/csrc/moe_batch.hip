@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe_impl {
 
 // ---------------------------------------------------------------------------
@@ -18,6 +20,50 @@ namespace moe_impl {
 // counts over the pairs, so the result does not depend on thread timing.
 constexpr int kGroupBlock = 1024;  // one wave per token for up to 16 tokens at a time
 
+// Counting sort of the P (token, expert) pairs whose experts are in pe[] (LDS,
+// P entries, visible to the whole workgroup) by expert id, pair order kept
+// inside an expert: g_pair holds the pairs grouped, g_expert the U distinct
+// experts ascending, g_start[g] the first position of group g (g_start[U] =
+// P), g_count[0] = U.  pless, pfirst and n_first are LDS scratch (n_first
+// zeroed before the caller's barrier).  The ranks are plain counts over the
+// pairs, so the result does not depend on thread timing.  The outputs may be
+// in LDS or in global memory; the caller synchronises before reading them.
+__device__ __forceinline__ void group_pairs(const int *pe, int P, int *pless, unsigned char *pfirst,
+                                            int &n_first, int32_t *g_pair, int32_t *g_expert,
+                                            int32_t *g_start, int32_t *g_count) {
+  const int nt = (int)blockDim.x;
+  int mine = 0;
+  for (int q = threadIdx.x; q < P; q += nt) {
+    const int e = pe[q];
+    int less = 0, before = 0;
+    for (int r = 0; r < P; ++r) {
+      const int f = pe[r];
+      less += f < e;
+      before += (r < q) & (f == e);
+    }
+    g_pair[less + before] = q;
+    pless[q] = less;
+    pfirst[q] = before == 0;
+    mine += before == 0;
+  }
+  atomicAdd(&n_first, mine);
+  __syncthreads();
+  for (int q = threadIdx.x; q < P; q += nt) {
+    if (!pfirst[q]) continue;
+    const int e = pe[q];
+    int g = 0;
+    for (int r = 0; r < P; ++r) g += pfirst[r] & (pe[r] < e);
+    g_expert[g] = e;
+    g_start[g] = pless[q];
+  }
+  if (threadIdx.x == 0) {
+    g_count[0] = n_first;
+    g_start[n_first] = P;
+  }
+}
+
+// One workgroup: the top-K of every token (wave w takes tokens w, w + 4, ...)
+// unless the selection is given, then the grouping of the T*K pairs.
 __global__ __launch_bounds__(kGroupBlock) void k_route_group(RouteGroupParams p) {
   __shared__ int pe[kMaxTokens * kMaxK];
   __shared__ int pless[kMaxTokens * kMaxK];
@@ -39,36 +85,41 @@ __global__ __launch_bounds__(kGroupBlock) void k_route_group(RouteGroupParams p)
     }
   }
   __syncthreads();
-  const int P = p.T * p.K;
-  int mine = 0;
-  for (int q = threadIdx.x; q < P; q += kGroupBlock) {
-    const int e = pe[q];
-    int less = 0, before = 0;
-    for (int r = 0; r < P; ++r) {
-      const int f = pe[r];
-      less += f < e;
-      before += (r < q) & (f == e);
-    }
-    p.g_pair[less + before] = q;
-    pless[q] = less;
-    pfirst[q] = before == 0;
-    mine += before == 0;
-  }
-  atomicAdd(&n_first, mine);
-  __syncthreads();
-  for (int q = threadIdx.x; q < P; q += kGroupBlock) {
-    if (!pfirst[q]) continue;
-    const int e = pe[q];
-    int g = 0;
-    for (int r = 0; r < P; ++r) g += pfirst[r] & (pe[r] < e);
-    p.g_expert[g] = e;
-    p.g_start[g] = pless[q];
-  }
-  if (threadIdx.x == 0) {
-    p.g_count[0] = n_first;
-    p.g_start[n_first] = P;
-  }
+  group_pairs(pe, p.T * p.K, pless, pfirst, n_first, p.g_pair, p.g_expert, p.g_start, p.g_count);
 }
+
+
+// The grouped gate/up kernel's own grouping (batches of at most
+// kGroupInKernel pairs): every workgroup sorts the pairs into LDS from the
+// selection, so no grouping launch sits between the top-K and the gate/up.
+// (a multiple of 16 bytes: the kernel's dynamic LDS, read with 16-byte
+// loads, starts right after it)
+struct alignas(16) GroupLds {
+  int pe[kGroupInKernel], pless[kGroupInKernel];
+  int32_t pair[kGroupInKernel], expert[kGroupInKernel], start[kGroupInKernel + 1], count;
+  unsigned char pfirst[kGroupInKernel];
+  int n_first;
+};
+static_assert(sizeof(GroupLds) % 16 == 0, "keeps the dynamic LDS after it 16-byte aligned");
+
+// The groups as the grouped kernels read them: in global memory (written by
+// k_route_group or by the gate/up kernel's workgroup 0), or in the gate/up
+// kernel's LDS.  Two types rather than one pointer that may point to either,
+// so that the LDS reads compile to LDS instructions: a flat load would also
+// count against the vector memory counter and wait for the weight rows
+// requested ahead of it.
+struct GlobalGroups {
+  const GroupedParams &p;
+  __device__ int expert(int g) const { return p.g_expert[g]; }
+  __device__ int start(int g) const { return p.g_start[g]; }
+  __device__ int pair(int i) const { return p.g_pair[i]; }
+};
+struct LdsGroups {
+  const GroupLds &gl;
+  __device__ int expert(int g) const { return gl.expert[g]; }
+  __device__ int start(int g) const { return gl.start[g]; }
+  __device__ int pair(int i) const { return gl.pair[i]; }
+};
 
 // the group of a work item: its expert (or the shared one) and its tokens;
 // lane j < n holds the j-th (pair, token) of the group
@@ -85,7 +136,9 @@ __device__ __forceinline__ int n_work_items(const GroupedParams &p, int U) {
   return ((p.do_shared ? p.shared_split : 0) + U) * p.tiles;
 }
 
-__device__ __forceinline__ GroupRef item_ref(const GroupedParams &p, int item, int U, int &tile) {
+template <class Groups>
+__device__ __forceinline__ GroupRef item_ref(const GroupedParams &p, const Groups &gv, int item,
+                                             int U, int &tile) {
   GroupRef r;
   const int lane = lane_id();
   const int n_sh = p.do_shared ? p.shared_split * p.tiles : 0;
@@ -104,10 +157,10 @@ __device__ __forceinline__ GroupRef item_ref(const GroupedParams &p, int item, i
     const int g = q / p.tiles;
     tile = q - g * p.tiles;
     r.shared = false;
-    r.id = wave_uniform(p.g_expert[g]);
-    const int s0 = wave_uniform(p.g_start[g]);
-    r.n = wave_uniform(p.g_start[g + 1]) - s0;
-    r.pair = lane < r.n ? p.g_pair[s0 + lane] : 0;
+    r.id = wave_uniform(gv.expert(g));
+    const int s0 = wave_uniform(gv.start(g));
+    r.n = wave_uniform(gv.start(g + 1)) - s0;
+    r.pair = lane < r.n ? gv.pair(s0 + lane) : 0;
     r.tok = r.pair / p.K;
   }
   return r;
@@ -188,14 +241,44 @@ constexpr int kGroupTB = 4;  // tokens that share one unpacking of a code chunk
 // consecutive row tiles of one expert group, so the tokens' activations are
 // staged into LDS once per workgroup, tok_batch tokens at a time, and read
 // there by all four waves.
-template <int BITS, int NCH, int NPASS, int XS>
+// GL: the kernel groups the (token, expert) pairs itself, into LDS
+// (p.group_idx set, at most kGroupInKernel pairs)
+template <int BITS, int NCH, int NPASS, int XS, bool GL>
 __global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedParams p) {
   extern __shared__ uint32_t lds_x[];
   constexpr bool XF32 = XS != XS_BF16;
   using Stage = XStage<BITS, XF32>;
   constexpr int CS = lds_chunk_words<Stage>();
   const int wv = wave_uniform(threadIdx.x >> 6);
-  const int U = p.do_routed ? wave_uniform(p.g_count[0]) : 0;
+  __shared__ GroupLds gl;
+  int U = 0;
+  if (GL && p.do_routed) {  // launch-uniform
+    const int P = p.T * p.K;
+    if (threadIdx.x == 0) gl.n_first = 0;
+    for (int q = threadIdx.x; q < P; q += kBlock) gl.pe[q] = p.group_idx[q];
+    __syncthreads();
+    group_pairs(gl.pe, P, gl.pless, gl.pfirst, gl.n_first, gl.pair, gl.expert, gl.start, &gl.count);
+    __syncthreads();
+    U = gl.count;
+    if (blockIdx.x == 0) {  // the groups for the down kernel (the workspace
+                            // arrays a grouping launch would have written)
+      int32_t *g_pair = const_cast<int32_t *>(p.g_pair), *g_expert = const_cast<int32_t *>(p.g_expert);
+      int32_t *g_start = const_cast<int32_t *>(p.g_start), *g_count = const_cast<int32_t *>(p.g_count);
+      for (int q = threadIdx.x; q < P; q += kBlock) {
+        g_pair[q] = gl.pair[q];
+        if (q < U) g_expert[q] = gl.expert[q];
+      }
+      for (int q = threadIdx.x; q <= U; q += kBlock) g_start[q] = gl.start[q];
+      if (threadIdx.x == 0) g_count[0] = U;
+    }
+  } else if (p.do_routed) {
+    U = wave_uniform(p.g_count[0]);
+  }
+  using Groups = typename std::conditional<GL, LdsGroups, GlobalGroups>::type;
+  const Groups gv = [&] {
+    if constexpr (GL) return LdsGroups{gl};
+    else return GlobalGroups{p};
+  }();
   const int n_items = n_work_items(p, U);
   const RowMap m = row_map<BITS>(p.H);
   const int cpr = m.cpr;
@@ -207,7 +290,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedParams p) {
   int nrow0 = 0;
   auto fetch = [&](int item, GUTile<BITS, NCH, NPASS> &t, GroupRef &r, int &row0) {
     int tile;
-    r = item_ref(p, item < n_items ? item : 0, U, tile);
+    r = item_ref(p, gv, item < n_items ? item : 0, U, tile);
     row0 = (tile * 4 + wv) * p.rows_per_wave;
     const bool v = r.shared ? true : (r.id >= 0 && r.id < p.E);
     const uint8_t *rec = r.shared ? p.shared_rec : p.experts + (size_t)(v ? r.id : 0) * p.stride;
@@ -318,6 +401,7 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedParams p) {
   constexpr int PC = NC + kLdsPad;
   const int wv = wave_uniform(threadIdx.x >> 6);
   const int U = p.do_routed ? wave_uniform(p.g_count[0]) : 0;
+  const GlobalGroups gv{p};
   const int n_items = n_work_items(p, U);
   const RowMap m = row_map<BITS>(p.I);
   const int tok_floats = (p.I / NC) * PC;
@@ -326,7 +410,7 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedParams p) {
   int nrow0 = 0;
   auto fetch = [&](int item, DnTile<BITS, NCH, NPASS> &t, GroupRef &r, int &row0) {
     int tile;
-    r = item_ref(p, item < n_items ? item : 0, U, tile);
+    r = item_ref(p, gv, item < n_items ? item : 0, U, tile);
     row0 = (tile * 4 + wv) * p.rows_per_wave;
     const bool v = r.shared ? true : (r.id >= 0 && r.id < p.E);
     const uint8_t *rec = r.shared ? p.shared_rec : p.experts + (size_t)(v ? r.id : 0) * p.stride;
@@ -447,8 +531,12 @@ hipError_t launch_gateup_grouped(const GroupedParams &p0, hipStream_t s) {
     const size_t per_tok = (size_t)cpr * lds_chunk_words<XStage<BITS, XS != XS_BF16>>() * 4;   \
     p.tok_batch = tok_batch_for(per_tok, p.T);                                                 \
     const size_t lds = per_tok * p.tok_batch;                                                  \
-    MOE_DISPATCH_G(nch, npass, MOE_LAUNCH((k_gateup_grouped<BITS, NCH_, NP_, XS>), grid,        \
-                                          dim3(kBlock), lds, s, p));                           \
+    if (p.group_idx)                                                                           \
+      MOE_DISPATCH_G(nch, npass, MOE_LAUNCH((k_gateup_grouped<BITS, NCH_, NP_, XS, true>), grid, \
+                                            dim3(kBlock), lds, s, p));                         \
+    else                                                                                       \
+      MOE_DISPATCH_G(nch, npass, MOE_LAUNCH((k_gateup_grouped<BITS, NCH_, NP_, XS, false>), grid, \
+                                            dim3(kBlock), lds, s, p));                         \
   } while (0)
   if (p.bits == 4) {
     if (p.xsrc == XS_BF16) { MOE_GG(4, XS_BF16); } else { MOE_GG(4, XS_F32); }

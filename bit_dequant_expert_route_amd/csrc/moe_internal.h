@@ -114,7 +114,12 @@ struct GroupedParams {
   int rows_per_wave, tiles;       // set by the launcher (tiles of four waves)
   int tok_batch;                  // tokens staged in LDS at a time (launcher)
   int shared_split;               // token ranges of the shared expert's items (launcher)
+  // gate/up only: the selection [T][K]; when set (T K <= kGroupInKernel) the
+  // kernel groups the pairs itself and its workgroup 0 writes g_* for the
+  // down kernel, instead of a grouping launch before it
+  const int32_t *group_idx;
 };
+constexpr int kGroupInKernel = 128;
 hipError_t launch_gateup_grouped(const GroupedParams &p, hipStream_t s);
 hipError_t launch_down_grouped(const GroupedParams &p, hipStream_t s);
 
