@@ -130,47 +130,76 @@ __device__ __forceinline__ void norm_to_lds(const float *h, int H, float *xl) {
 
 constexpr int kGdnInWaves = 8;
 
+// The grid holds as many workgroups as fit the CUs at once; each normalises
+// h once and its waves loop over units (rows_per_wave rows of one matrix),
+// unit u of a wave followed by u + (waves in the grid), each unit's rows
+// requested before the previous unit is computed.  (One unit per wave took
+// three rounds of workgroups at 4,096 rows per matrix, each round paying the
+// normalisation again: 19.2 us per block.)
 template <int BITS, int NCH, int NPASS>
 __global__ __launch_bounds__(64 * kGdnInWaves) void k_gdn_in(GdnInParams p) {
   extern __shared__ float xl[];
-  const int wave = wave_uniform(blockIdx.x * kGdnInWaves + (threadIdx.x >> 6));
+  const int wave0 = wave_uniform(blockIdx.x * kGdnInWaves + (threadIdx.x >> 6));
+  const int stride = (int)gridDim.x * kGdnInWaves;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     p.one_idx[0] = 0;
     p.one_w[0] = 1.0f;
     p.zero_sigma[0] = 0.0f;
   }
-  // wave -> matrix (0 q, 1 k, 2 v, 3 the gate rows) and its first row
+  // unit -> matrix (0 q, 1 k, 2 v, 3 the gate rows) and its first row
   const int rpw = p.rows_per_wave;
   const int wpm = (p.D + rpw - 1) / rpw;
-  const int mat = wave / wpm < 3 ? wave / wpm : 3;
-  const int row0 = (wave - mat * wpm) * rpw;
-  const int rows = mat < 3 ? p.D : 2 * p.n_heads;
-  const bool active = row0 < rows;
-  RecOffsets o2 = p.off;
-  o2.down_codes = (mat & 1) ? p.off.up_codes : p.off.gate_codes;
-  o2.down_sb = (mat & 1) ? p.off.up_sb : p.off.gate_sb;
-  const uint8_t *rec = mat < 2 ? p.rec_qko : p.rec_vab;
+  const int n_units = 3 * wpm + (2 * p.n_heads + rpw - 1) / rpw;
   const RowMap m = row_map<BITS>(p.H);
+  struct Unit {
+    int mat, row0, rows;
+    const uint8_t *rec;
+    RecOffsets off;
+  };
+  auto unit_of = [&](int u) {
+    Unit r;
+    r.mat = u / wpm < 3 ? u / wpm : 3;
+    r.row0 = (u - r.mat * wpm) * rpw;
+    r.rows = r.mat < 3 ? p.D : 2 * p.n_heads;
+    r.off = p.off;
+    r.off.down_codes = (r.mat & 1) ? p.off.up_codes : p.off.gate_codes;
+    r.off.down_sb = (r.mat & 1) ? p.off.up_sb : p.off.gate_sb;
+    r.rec = r.mat < 2 ? p.rec_qko : p.rec_vab;
+    return r;
+  };
+  int u = wave0;
+  Unit cu = unit_of(u < n_units ? u : 0);
   DnTile<BITS, NCH, NPASS> t;
-  down_load(t, rec, o2, active ? rows : 1, m, active ? row0 : 0);
+  down_load(t, cu.rec, cu.off, u < n_units && cu.row0 < cu.rows ? cu.rows : 1, m,
+            u < n_units && cu.row0 < cu.rows ? cu.row0 : 0);
   norm_to_lds<BITS, kGdnInWaves>(p.h, p.H, xl);
-  if (!active) return;
   XStage<BITS, true> xs[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = m.li + (j << m.lg);
     xs[j] = make_stage<BITS, XS_LDSPAD>(nullptr, xl, c < m.cpr ? c : 0);
   }
-  float acc[NPASS];
+  for (; u < n_units; u += stride) {  // wave-uniform
+    const int un = u + stride;
+    const Unit nu = unit_of(un < n_units ? un : 0);
+    const bool nvalid = un < n_units && nu.row0 < nu.rows;
+    DnTile<BITS, NCH, NPASS> tn;
+    if (un < n_units) down_load(tn, nu.rec, nu.off, nvalid ? nu.rows : 1, m, nvalid ? nu.row0 : 0);
+    if (cu.row0 < cu.rows) {
+      float acc[NPASS];
 #pragma unroll
-  for (int i = 0; i < NPASS; ++i) acc[i] = 0.f;
-  down_accumulate_staged<BITS, NCH, NPASS>(xs, m, rows, row0, true, 1.0f, t, acc);
-  float *out = p.proj + (size_t)mat * p.D;
+      for (int i = 0; i < NPASS; ++i) acc[i] = 0.f;
+      down_accumulate_staged<BITS, NCH, NPASS>(xs, m, cu.rows, cu.row0, true, 1.0f, t, acc);
+      float *out = p.proj + (size_t)cu.mat * p.D;
 #pragma unroll
-  for (int i = 0; i < NPASS; ++i) {
-    const float sum = seg_sum(acc[i], m.lg);
-    const int r = row0 + i * m.rpp + m.rip;
-    if (m.li == 0 && r < rows) out[r] = sum;
+      for (int i = 0; i < NPASS; ++i) {
+        const float sum = seg_sum(acc[i], m.lg);
+        const int r = cu.row0 + i * m.rpp + m.rip;
+        if (m.li == 0 && r < cu.rows) out[r] = sum;
+      }
+    }
+    t = tn;
+    cu = nu;
   }
 }
 
@@ -178,11 +207,18 @@ hipError_t launch_gdn_in(const GdnInParams &p0, hipStream_t s) {
   GdnInParams p = p0;
   const int nch = nch_for(p.H, p.bits);
   const int rpp = rpp_for(p.H, p.bits);
-  const int npass = clamp_pass(nch, rpp >= 2 ? 1 : 2);
+  // one pass of rows per unit: the waves loop over units, and the lighter
+  // tile lets two workgroups share a CU
+  const int npass = 1;
   p.rows_per_wave = npass * rpp;
   const int wpm = (p.D + p.rows_per_wave - 1) / p.rows_per_wave;
   const int waves = 3 * wpm + (2 * p.n_heads + p.rows_per_wave - 1) / p.rows_per_wave;
-  const dim3 grid((waves + kGdnInWaves - 1) / kGdnInWaves);
+  // at most the workgroups that fit the CUs at once: two per CU, one for the
+  // variants with more than 128 VGPRs (four 4-bit or two 2-bit chunks per lane)
+  const int per_cu = (nch >= 4 || (p.bits == 2 && nch >= 2)) ? 1 : 2;
+  int blocks = (waves + kGdnInWaves - 1) / kGdnInWaves;
+  if (blocks > kCUs * per_cu) blocks = kCUs * per_cu;
+  const dim3 grid(blocks);
   const int nc = 128 / p.bits;
   const size_t lds = (size_t)(p.H / nc) * (nc + kLdsPad) * sizeof(float);
 #define MOE_GI(BITS)                                                                            \
