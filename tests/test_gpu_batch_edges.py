@@ -2,7 +2,9 @@
 against the oracle per token: 2-bit experts, a 2-bit layer with a 4-bit shared
 expert and fp32 activations (the shared expert's own grouped launches), rows
 that do not fill a wave (H, I multiples of 64 but not of 128), the largest K,
-the largest expert count, and the widest rows (four code chunks per lane)."""
+the largest expert count, the widest rows (four code chunks per lane), and
+batches of more than 128 (token, expert) pairs, which take the separate
+grouping launch."""
 import pytest
 
 from bit_dequant_expert_route_amd import synth
@@ -21,6 +23,10 @@ EDGE = {
     "e1024": (C("batch_e1024", 128, 64, 1024, 4, 4, 4, "bf16", "bf16", "bf16", n_tokens=5), 12),
     "wide4": (C("batch_wide4", 8192, 64, 16, 2, 4, 4, "bf16", "bf16", "bf16", n_tokens=3), 4),
     "wide2": (C("batch_wide2", 8192, 128, 16, 2, 2, 2, "bf16", "bf16", "bf16", n_tokens=3), 4),
+    # more than 128 (token, expert) pairs: the separate grouping launch
+    # (up to 128 the gate/up kernel groups the pairs itself)
+    "pairs256": (C("batch_pairs256", 128, 64, 64, 8, 4, 4, "bf16", "bf16", "bf16", n_tokens=32), 40),
+    "pairs129": (C("batch_pairs129", 128, 64, 64, 3, 4, 4, "bf16", "bf16", "bf16", n_tokens=43), 40),
 }
 
 
