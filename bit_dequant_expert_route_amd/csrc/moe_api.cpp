@@ -994,8 +994,12 @@ static int stack_run(const moe_layer_t *layers, int n_layers, const uint16_t *up
   auto upd = [&](int l) { return updates ? updates + (size_t)l * H : nullptr; };
   MOE_TRY_HIP(timed(s, MOE_KERNEL_OTHER, [&] { return launch_zero(acc[0], 2 * nacc * sizeof(double), s); }),
               "accumulator zero launch");
-  // layer 0's input v = h + u_0 and its routing sums
-  float *v = buf[1];
+  // layer 0's input v = h + u_0 and its routing sums.  The layers' outputs
+  // alternate between h and the ping-pong buffer; v starts in h (k_partials
+  // reads and writes each element in one thread, so in place is safe) when
+  // the layer count is even, else in the other buffer, so that the last
+  // layer's output lands in h and no copy follows.
+  float *v = (n_layers % 2 == 0) ? buf[0] : buf[1];
   PartialsParams pp;
   pp.H = (int)H;
   pp.E = L0->n_experts;
