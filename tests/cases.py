@@ -199,8 +199,13 @@ class GdnStackCase:
 
 
 def make_gdn_stack_case(cfg: synth.LayerConfig, seed: int, n_layers: int | None = None,
-                        renorm: bool = True, orc: oracle.Oracle | None = None) -> GdnStackCase:
+                        renorm: bool = True, orc: oracle.Oracle | None = None,
+                        attention=None) -> GdnStackCase:
+    """attention(l): whether layer l is a full-attention stand-in (no
+    linear-attention block, a bf16 update instead); every fourth layer unless
+    given."""
     orc = orc or oracle.get()
+    attention = attention or synth.is_attention_layer
     L = n_layers or cfg.n_layers
     H, nh, dh, gb = cfg.hidden, cfg.gdn_heads, cfg.gdn_head_dim, cfg.gdn_bits
     h = synth.stack_h0(cfg, seed).astype(np.float64)
@@ -209,7 +214,7 @@ def make_gdn_stack_case(cfg: synth.LayerConfig, seed: int, n_layers: int | None 
     for l in range(L):
         router = synth.router_weights(cfg, seed, l)
         gate = synth.shared_gate_vector(cfg, seed, l)
-        attn = synth.is_attention_layer(l)
+        attn = attention(l)
         rq = rv = None
         if not attn:
             rq, rv = synth.gdn_records(seed, l, H, nh, dh, gb)

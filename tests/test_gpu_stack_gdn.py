@@ -82,9 +82,9 @@ def _check(case, h, idx_log, w_log, states):
     return e
 
 
-def _run(cfg, seed, n_layers=None, graph_replays=0):
+def _run(cfg, seed, n_layers=None, graph_replays=0, attention=None):
     from bit_dequant_expert_route_amd import moe
-    case = make_gdn_stack_case(cfg, seed, n_layers)
+    case = make_gdn_stack_case(cfg, seed, n_layers, attention=attention)
     n_gdn = sum(s is not None for s in case.states0)
     log(f"gdn stack {cfg.name} seed {seed}: {case.n_layers} layers ({n_gdn} linear attention), "
         f"redraws {sum(case.attempts)}")
@@ -152,6 +152,15 @@ GDN_EDGE = {
 @pytest.mark.parametrize("name", list(GDN_EDGE))
 def test_gdn_stack_edges(name):
     _run(GDN_EDGE[name], 17, graph_replays=1)
+
+
+def test_gdn_stack_attention_first():
+    """Layers 0, 1 and 4 without a linear-attention block: layer 0 takes its
+    routing sums from the partials kernel, layer 1 from layer 0's combine
+    (one such layer feeding the next) and layer 4 from the combine of a
+    layer with a block."""
+    _run(synth.CONFIGS["tiny_stack_gdn"], 23, n_layers=6, graph_replays=1,
+         attention=lambda l: l in (0, 1, 4))
 
 
 def test_q4_gdn_stack_full_shape():
