@@ -892,6 +892,7 @@ static int gdn_block(const moe_layer_t *L, const moe_gdn_layer_t *g, const float
   dp.idx = one_idx;
   dp.w = one_w;
   dp.K = 1;
+  dp.fixed_first = 1;
   dp.sigma = zero_sigma;
   dp.h_routed = o;
   dp.h_shared = nullptr;

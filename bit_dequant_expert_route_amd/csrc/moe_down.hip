@@ -78,10 +78,15 @@ __global__ __launch_bounds__(64 * WAVES, (MAXK == 1 && BITS == 4) ? 4 : 1) void 
   // way).
   int ids[MAXK];
   float wk[MAXK];
+  if (MAXK == 1 && p.fixed_first) {  // uniform
+    ids[0] = 0;
+    wk[0] = 1.0f;
+  } else {
 #pragma unroll
-  for (int k = 0; k < MAXK; ++k) {
-    ids[k] = k < p.K ? p.idx[k] : -2;
-    wk[k] = k < p.K ? p.w[k] : 0.f;
+    for (int k = 0; k < MAXK; ++k) {
+      ids[k] = k < p.K ? p.idx[k] : -2;
+      wk[k] = k < p.K ? p.w[k] : 0.f;
+    }
   }
   DnTile<BITS, NCH, NPASS> ts;
   if constexpr (SHARED_IN && EPI) {
@@ -355,6 +360,7 @@ hipError_t launch_down(const DownParams &p0, hipStream_t s) {
     // projection): tiles for one expert only, so the kernel keeps few
     // registers and its waves fit the CUs in one round
     const bool k1 = p.K == 1 && !shared_in;
+    if (p.fixed_first && !k1) return hipErrorInvalidValue;
     if (bits == 4) {
       if (shared_in) { if (k4) MOE_DC(4, 4, true); else MOE_DC(4, 8, true); }
       else { if (k1) MOE_DC(4, 1, false); else if (k4) MOE_DC(4, 4, false); else MOE_DC(4, 8, false); }

@@ -208,6 +208,10 @@ struct DownParams {
   const int32_t *idx;             // [K]
   const float *w;                 // [K]
   int K;
+  // K == 1 with weight 1 on expert 0, known to the launcher (the
+  // linear-attention block's output projection): idx and w are not read, so
+  // the rows are requested without waiting for an id
+  int fixed_first;
   const float *sigma;             // [1]
   const float *h_routed;          // [K][I]
   const float *h_shared;          // [I]
